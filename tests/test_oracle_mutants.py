@@ -1,0 +1,77 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a temporary copy of the oracle's C source
+(a dropped term, a wrong index, a wrong sign, a wrong exponent bias, the
+wrong tie rule), builds it with gcc, swaps it in for the real library and
+checks that at least one pin test fails.  Everything runs on the CPU.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_decode_round as T1
+from tests import test_oracle_gemm as T2
+from tests._cases import golden_cases
+
+MUTANTS = {
+    "dropped_last_term_of_group": ("for (int64_t k = k0; k < k1; ++k)", "for (int64_t k = k0; k + 1 < k1; ++k)"),
+    "a_scale_always_group0": ("(double)a_s[m * G + g]", "(double)a_s[m * G]"),
+    "b_scale_always_block0": ("(double)b_s[(n / ORACLE_GROUP) * G + g]", "(double)b_s[g]"),
+    "b_scale_indexed_by_row_mod": ("(double)b_s[(n / ORACLE_GROUP) * G + g]", "(double)b_s[(n % 2 < (N + 127) / 128 ? n % 2 : 0) * G + g]"),
+    "wrong_sign_of_fold": ("acc += p * s;", "acc -= p * s;"),
+    "subnormal_scale": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "exponent_bias": ("(int)e - 7", "(int)e - 8"),
+    "ties_away_from_zero": ("nearbyint(x / q)", "round(x / q)"),
+    "bf16_precision": ("round_to_format(v, 8, -126, 127)", "round_to_format(v, 9, -126, 127)"),
+    "fp16_exponent_bias": ("(unsigned)(E + 15) << 10", "(unsigned)(E + 14) << 10"),
+}
+
+PINS = [
+    T1.test_decode_matches_torch_all_codes,
+    T1.test_decode_format_landmarks,
+    T1.test_round_fp32_matches_numpy,
+    T1.test_round_fp16_matches_numpy,
+    T1.test_round_bf16_against_value_set,
+    T1.test_round_bf16_is_one_step_from_fp64,
+    lambda: [T2.test_handworked_cases(c) for c in golden_cases()],
+    lambda: T2.test_brute_force_exact_rational(1, 3, 4, 128),
+    lambda: T2.test_brute_force_exact_rational(4, 1, 130, 128),
+    T2.test_integer_mode_is_exact,
+    lambda: T2.test_matches_numpy_blas_of_dequantised_operands(37, 300, 512),
+    T2.test_identity_weight_exposes_every_code,
+    T2.test_row_and_column_block_locality,
+]
+
+
+def _build_mutant(tmp, old, new):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "fp8bg_oracle.c")).read()
+    assert src.count(old) == 1, old
+    path = os.path.join(tmp, "m.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = os.path.join(tmp, "m.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    path, "-o", lib, "-lm"], check=True)
+    return lib
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    old, new = MUTANTS[name]
+    with tempfile.TemporaryDirectory() as tmp:
+        lib_path = _build_mutant(tmp, old, new)
+        real = oracle._load()
+        monkeypatch.setattr(oracle, "_LIB_PATH", lib_path)
+        monkeypatch.setattr(oracle, "_lib", None)
+        oracle._load()
+        caught = []
+        for pin in PINS:
+            try:
+                pin()
+            except Exception:
+                caught.append(getattr(pin, "__name__", "lambda"))
+        monkeypatch.setattr(oracle, "_lib", real)
+    assert caught, f"no pin caught mutant {name}"
