@@ -1,0 +1,249 @@
+"""Benchmark of the block-scaled FP8 GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the whole hot path, fp8_block_gemm_ex (dispatcher +
+kernel, with split-K's fixed-order reduction inside the kernel), on one
+batch of synthetic input of the named workload (default: the decode shape
+M=64, N=512, K=4096, bf16 output).  Inputs sit in HBM before timing starts;
+consecutive steps rotate over enough input copies (> 2x the 256 MB MALL) that
+every step streams its operands from HBM, not from cache.  Steps are issued
+from HIP graphs (captured through torch) so that host launch cost does not
+hide the GPU time of a microsecond-scale kernel.  The timed region is
+bracketed by device synchronisation and by HIP events on the stream the
+kernels run on; ms_per_step and the roofline's per-launch duration come
+from those events.
+
+Prints ONE JSON line (the benchmark contract), plus, on rank 0 at N=1, the
+CPU oracle timed on a bounded sample of the same workload.
+
+Other modes (for profiles):
+  --sweep FILE        every workload and sweep point, one JSON line each, to FILE
+  --copy-bytes B      only a plain device copy of B bytes (calibrates HBM counters)
+  --no-graph          launch each step eagerly (for counter collection)
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+MALL_BYTES = 256 << 20
+METRIC = "TFLOP/s and % of roofline (HBM or FP8 MFMA) per (M,N,K), 1×MI355X"
+
+
+def alg_bytes(M, N, K, out_bytes):
+    """Each input read once, C written once (split-K partials are overhead)."""
+    G, NB = K // 128, (N + 127) // 128
+    return M * K + N * K + 4 * M * G + 4 * NB * G + M * N * out_bytes
+
+
+def make_device_copies(w, M, copies, torch, W):
+    d = W.make_workload(w, M)
+    dev = torch.device("cuda:0")
+    base = {
+        "A": torch.from_numpy(d["A"]).to(dev).view(torch.float8_e4m3fn),
+        "a_s": torch.from_numpy(d["a_s"]).to(dev),
+        "B": torch.from_numpy(d["B"]).to(dev).view(torch.float8_e4m3fn),
+        "b_s": torch.from_numpy(d["b_s"]).to(dev),
+    }
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+    return d, sets
+
+
+def run_workload(args, w, M, out_name, torch, fbg, W, steps, warmup, use_graph=True,
+                 variant="auto", split_k=0, cfg=None):
+    out_dtype = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[out_name]
+    out_bytes = 4 if out_name == "fp32" else 2
+    N, K = w.N, w.K
+    per_copy = M * K + N * K + 4 * M * (K // 128) + 4 * ((N + 127) // 128) * (K // 128) + M * N * out_bytes
+    copies = max(1, min(args.max_copies, -(-2 * MALL_BYTES // per_copy)))
+    d, sets = make_device_copies(w, M, copies, torch, W)
+    outs = [torch.empty((M, N), dtype=out_dtype, device="cuda:0") for _ in range(copies)]
+    if cfg is not None:
+        os.environ["FBG_FORCE_CONFIG"] = str(cfg)
+    plan = fbg.plan(M, N, K, out_dtype, torch.cuda.get_device_properties(0).multi_processor_count,
+                    variant, split_k)
+    if cfg is not None:
+        plan["config"] = cfg
+    ws = torch.zeros(max(fbg.workspace_size(M, N, K, variant, split_k), 16), dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.Stream()
+
+    def step(i):
+        s = sets[i % copies]
+        fbg.gemm(s["A"], s["a_s"], s["B"], s["b_s"], out_dtype=out_dtype, out=outs[i % copies],
+                 workspace=ws, stream=stream, variant=variant, split_k=split_k)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i)
+    torch.cuda.synchronize()
+
+    plan_seq = []
+    if use_graph:
+        # Each graph holds `chunk` consecutive steps (one pass over the input
+        # copies); the chunks executed add up to exactly `steps`.
+        chunk = min(steps, copies)
+        sizes = [chunk] * (steps // chunk) + ([steps % chunk] if steps % chunk else [])
+        graphs = {}
+        for n in sorted(set(sizes)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n):
+                    step(i)
+            graphs[n] = g
+        plan_seq = [graphs[n] for n in sizes]
+        with torch.cuda.stream(stream):   # replay() launches on the current stream
+            for g in graphs.values():     # one untimed replay of each graph
+                g.replay()
+        torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        if use_graph:
+            for g in plan_seq:
+                g.replay()
+        else:
+            for i in range(steps):
+                step(i)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / steps
+    flops = 2 * M * N * K
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    nbytes = alg_bytes(M, N, K, out_bytes)
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    bound = "hbm" if flops / nbytes < FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / FP8_PEAK_TFLOPS, 4)}
+    if cfg is not None:
+        os.environ.pop("FBG_FORCE_CONFIG", None)
+    return {"d": d, "plan": plan, "ms_per_step": ms_per_step, "tflops": tflops, "gbs": gbs, "roof": roof,
+            "copies": copies, "wall_s": wall, "alg_bytes": nbytes}
+
+
+def cpu_baseline(d, flops_per_call, budget_s=12.0):
+    """The oracle as it stands, on the host's cores, repeated over the full
+    workload until about `budget_s` of CPU time has passed."""
+    import oracle
+    oracle.block_gemm(d["A"][:1], d["a_s"][:1], d["B"], d["b_s"])  # load the library
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.block_gemm(d["A"], d["a_s"], d["B"], d["b_s"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    return {"value": round(reps * flops_per_call / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"full workload GEMM (fp64 oracle, E4M3 decode) repeated {reps}x in {el:.1f} s"}
+
+
+def copy_only(nbytes, torch, reps=5):
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4096)
+    ap.add_argument("--warmup", type=int, default=256)
+    ap.add_argument("--workload", default="decode_64x512x4096")
+    ap.add_argument("--out", default=None, help="output dtype (default: the workload's first)")
+    ap.add_argument("--M", type=int, default=None, help="a sweep point of the workload")
+    ap.add_argument("--max-copies", type=int, default=1024)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sweep", default=None)
+    ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--variant", default="auto", help="force a kernel variant (tuning)")
+    ap.add_argument("--split", type=int, default=0, help="force a split-K count (tuning)")
+    ap.add_argument("--cfg", type=int, default=None, help="force a tile configuration (tuning)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note "
+                                   "(N-, M- or K-sharding of the GEMM), not a measured path",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    if args.copy_bytes:
+        copy_only(args.copy_bytes, torch)
+        return
+    import block_scaled_fp8_gemm_amd as fbg
+    import workloads as W
+    fbg.load()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+
+    if args.sweep:
+        with open(args.sweep, "w") as f:
+            for name, w in W.WORKLOADS.items():
+                for M in (w.M,) + tuple(m for m in w.sweep_M if m != w.M):
+                    for out in w.out_dtypes:
+                        steps = 200 if w.flops > 1e11 else 2048
+                        r = run_workload(args, w, M, out, torch, fbg, W, steps, 20, not args.no_graph)
+                        line = {"workload": name, "M": M, "N": w.N, "K": w.K, "out": out,
+                                "variant": r["plan"]["variant_name"], "cfg": r["plan"]["config"],
+                                "split_k": r["plan"]["split_k"], "grid": r["plan"]["grid"],
+                                "us": round(r["ms_per_step"] * 1e3, 3), "tflops": round(r["tflops"], 2),
+                                "gbs": round(r["gbs"], 1), "roofline": r["roof"], "copies": r["copies"]}
+                        f.write(json.dumps(line) + "\n")
+                        f.flush()
+                        print(json.dumps(line), flush=True)
+        return
+
+    w = W.WORKLOADS[args.workload]
+    M = args.M if args.M is not None else w.M
+    out = args.out or w.out_dtypes[0]
+    r = run_workload(args, w, M, out, torch, fbg, W, args.steps, args.warmup, not args.no_graph,
+                     args.variant, args.split, args.cfg)
+    roof = dict(r["roof"])
+    roof["traffic"] = None
+    line = {
+        "metric": METRIC,
+        "value": round(r["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "N": w.N, "K": w.K, "out_dtype": out,
+                   "variant": r["plan"]["variant_name"], "tile": [r["plan"]["tile_m"], r["plan"]["tile_n"]],
+                   "split_k": r["plan"]["split_k"], "grid": r["plan"]["grid"],
+                   "input_copies": r["copies"], "graphs": not args.no_graph},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(r["d"], 2 * M * w.N * w.K)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,152 @@
+"""Python binding of libfp8bg.so, the gfx950 block-scaled FP8 GEMM library.
+
+Argument marshalling only: every step of the GEMM runs in the library's HIP
+kernels; torch supplies device memory and the current stream.  The C ABI is
+declared in include/fp8bg.h.
+
+    C[m,n] = sum_g a_s[m,g] * b_s[n//128,g] * sum_{k in g} A[m,k] * B[n,k]
+
+(FlagGems-vllm PR #693, "feat: optimize w8a8 block fp8 matmul for Hopper",
+section "Description".)  If the library is not built, load() raises: there is
+no fallback of any kind.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8bg.so")
+
+SUCCESS, INVALID_VALUE, UNSUPPORTED, OUT_OF_MEMORY, HIP_ERROR = 0, 1, 2, 3, 4
+VARIANTS = {"auto": 0, "generic": 1, "short_k256": 2, "swap_ab": 3, "swap_ab_splitk": 4}
+VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
+OUT_CODES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
+OUT_DTYPES = {v: k for k, v in OUT_CODES.items()}
+FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)
+
+
+class FP8BGError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("split_k", ctypes.c_int32), ("waves", ctypes.c_int32), ("config", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+
+_lib = None
+_vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+
+def load():
+    """Loads libfp8bg.so (built in-tree by __graft_entry__.build()); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.fp8_block_gemm.restype = _int
+    lib.fp8_block_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]
+    lib.fp8_block_gemm_ex.restype = _int
+    lib.fp8_block_gemm_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp,
+                                      _int, _int, _vp, _sz]
+    lib.fp8_block_gemm_workspace_size.restype = _sz
+    lib.fp8_block_gemm_workspace_size.argtypes = [_i64, _i64, _i64, _int, _int]
+    lib.fp8_block_gemm_plan.restype = _int
+    lib.fp8_block_gemm_plan.argtypes = [_i64, _i64, _i64, _int, _int, _int, _int, ctypes.POINTER(Plan)]
+    lib.fp8_block_gemm_status_string.restype = ctypes.c_char_p
+    lib.fp8_block_gemm_status_string.argtypes = [_int]
+    lib.fp8_block_gemm_version.restype = _int
+    lib.fp8_block_gemm_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().fp8_block_gemm_status_string(int(status)).decode()
+
+
+def _variant_code(variant) -> int:
+    return VARIANTS[variant] if isinstance(variant, str) else int(variant)
+
+
+def _out_code(out_dtype) -> int:
+    if isinstance(out_dtype, int):
+        return out_dtype
+    return OUT_CODES[out_dtype]
+
+
+def plan(M: int, N: int, K: int, out_dtype=torch.bfloat16, cu_count: int = 256,
+         variant="auto", split_k: int = 0) -> dict:
+    """The dispatcher's decision (pure host call; works without a GPU)."""
+    p = Plan()
+    st = load().fp8_block_gemm_plan(M, N, K, _out_code(out_dtype), cu_count, _variant_code(variant),
+                                    split_k, ctypes.byref(p))
+    if st != SUCCESS:
+        raise FP8BGError(st, "fp8_block_gemm_plan")
+    d = {f: getattr(p, f) for f, _ in Plan._fields_}
+    d["variant_name"] = VARIANT_NAMES.get(p.variant, "none")
+    return d
+
+
+def workspace_size(M: int, N: int, K: int, variant="auto", split_k: int = 0) -> int:
+    n = load().fp8_block_gemm_workspace_size(M, N, K, _variant_code(variant), split_k)
+    if n == ctypes.c_size_t(-1).value:
+        raise FP8BGError(INVALID_VALUE, "fp8_block_gemm_workspace_size")
+    return int(n)
+
+
+def _check(t, name, dtypes, shape, device):
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def gemm(A: torch.Tensor, a_s: torch.Tensor, B: torch.Tensor, b_s: torch.Tensor,
+         out_dtype=torch.bfloat16, out: torch.Tensor = None, variant="auto", split_k: int = 0,
+         workspace: torch.Tensor = None, stream: torch.cuda.Stream = None) -> torch.Tensor:
+    """C = block-scaled A @ B^T on the current stream (or `stream`).
+
+    A [M,K] and B [N,K]: float8_e4m3fn (or uint8 holding E4M3 codes);
+    a_s [M, K/128], b_s [ceil(N/128), K/128]: float32; all contiguous on one
+    GPU.  variant/split_k force a kernel (see include/fp8bg.h); workspace is an
+    optional caller-owned byte buffer for split-K whose counter area is zero.
+    """
+    lib = load()
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape
+    N = B.shape[0]
+    G, NB = (K + 127) // 128, (N + 127) // 128
+    dev = A.device
+    _check(A, "A", FP8_DTYPES, (M, K), dev)
+    _check(B, "B", FP8_DTYPES, (N, K), dev)
+    _check(a_s, "a_s", (torch.float32,), (M, G), dev)
+    _check(b_s, "b_s", (torch.float32,), (NB, G), dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    else:
+        _check(out, "out", (out_dtype,), (M, N), dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    v, code = _variant_code(variant), _out_code(out_dtype)
+    if v == 0 and split_k == 0 and workspace is None:
+        st = lib.fp8_block_gemm(A.data_ptr(), a_s.data_ptr(), B.data_ptr(), b_s.data_ptr(), out.data_ptr(),
+                                M, N, K, code, s.cuda_stream)
+    else:
+        wp, wn = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
+            if workspace is not None else (None, 0)
+        st = lib.fp8_block_gemm_ex(A.data_ptr(), a_s.data_ptr(), B.data_ptr(), b_s.data_ptr(), out.data_ptr(),
+                                   M, N, K, code, s.cuda_stream, v, split_k, wp, wn)
+    if st != SUCCESS:
+        raise FP8BGError(st, "fp8_block_gemm")
+    return out

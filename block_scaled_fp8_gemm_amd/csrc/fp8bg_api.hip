@@ -1,0 +1,190 @@
+// C-ABI entry points: argument validation, the dispatcher's plan, split-K
+// workspace handling and kernel launch.  See include/fp8bg.h for the
+// contract of each function.
+#include <atomic>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "fp8bg.h"
+#include "fp8bg_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not yet queried
+
+int device_cu_count(int* status) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    *status = FBG_ERROR_HIP;
+    return 0;
+  }
+  if (dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cu = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) {
+    *status = FBG_ERROR_HIP;
+    return 0;
+  }
+  if (dev < kMaxDevices) g_cu_count[dev].store(cu, std::memory_order_relaxed);
+  return cu;
+}
+
+bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+int elem_size(int out_dtype) { return out_dtype == FBG_OUT_FP32 ? 4 : 2; }
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// FBG_FORCE_CONFIG=<index>: tests and benchmarks pin the tile configuration
+// of the chosen variant (read on every call so a test can change it).
+int forced_config() {
+  const char* v = getenv("FBG_FORCE_CONFIG");
+  return (v && v[0]) ? atoi(v) : -1;
+}
+
+// Pure host checks, made before any HIP call.
+int validate(const void* A, const float* a_s, const void* B, const float* b_s, const void* C, int64_t M,
+             int64_t N, int64_t K, int out_dtype) {
+  if (M < 0 || N < 0 || K < 0) return FBG_ERROR_INVALID_VALUE;
+  if (out_dtype != FBG_OUT_BF16 && out_dtype != FBG_OUT_FP16 && out_dtype != FBG_OUT_FP32)
+    return FBG_ERROR_INVALID_VALUE;
+  if (K % 128 != 0) return FBG_ERROR_UNSUPPORTED;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return FBG_ERROR_UNSUPPORTED;
+  const int64_t G = K / 128, NB = (N + 127) / 128;
+  const int64_t bytesA = M * K, bytesB = N * K, bytesAs = M * G * 4, bytesBs = NB * G * 4;
+  const int64_t bytesC = M * N * elem_size(out_dtype);
+  if ((bytesA > 0 && !A) || (bytesB > 0 && !B) || (bytesAs > 0 && !a_s) || (bytesBs > 0 && !b_s) ||
+      (bytesC > 0 && !C))
+    return FBG_ERROR_INVALID_VALUE;
+  if (overlaps(C, bytesC, A, bytesA) || overlaps(C, bytesC, B, bytesB) || overlaps(C, bytesC, a_s, bytesAs) ||
+      overlaps(C, bytesC, b_s, bytesBs))
+    return FBG_ERROR_INVALID_VALUE;
+  if ((bytesA > 0 && !aligned(A, 16)) || (bytesB > 0 && !aligned(B, 16)) || (bytesAs > 0 && !aligned(a_s, 4)) ||
+      (bytesBs > 0 && !aligned(b_s, 4)) || (bytesC > 0 && !aligned(C, (uintptr_t)elem_size(out_dtype))))
+    return FBG_ERROR_UNSUPPORTED;
+  return FBG_SUCCESS;
+}
+
+int launch_plan(const fbg_plan& p, const fbg::GemmArgs& args, void* ws, int64_t M, int64_t N) {
+  hipError_t e = hipSuccess;
+  switch (p.variant) {
+    case FBG_VARIANT_GENERIC:
+      e = fbg::launch_generic(args, p.config, p.grid, 8);
+      break;
+    case FBG_VARIANT_SHORT_K256:
+      e = fbg::launch_short_k256(args, p.config, p.grid);
+      break;
+    case FBG_VARIANT_SWAP_AB:
+    case FBG_VARIANT_SWAP_AB_SPLITK: {
+      float* partial = nullptr;
+      unsigned* counters = nullptr;
+      if (p.split_k > 1) {
+        partial = static_cast<float*>(ws);
+        counters = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + fbg::workspace_counter_offset(p, M, N));
+      }
+      e = fbg::launch_swap(args, p.config, p.grid, p.split_k, partial, counters);
+      break;
+    }
+    default:
+      return FBG_ERROR_INVALID_VALUE;
+  }
+  return e == hipSuccess ? FBG_SUCCESS : FBG_ERROR_HIP;
+}
+
+}  // namespace
+
+extern "C" int fp8_block_gemm_ex(const void* A, const float* a_s, const void* B, const float* b_s, void* C, int64_t M,
+                                 int64_t N, int64_t K, int out_dtype, void* stream_, int variant, int split_k,
+                                 void* workspace, size_t workspace_size) {
+  int st = validate(A, a_s, B, b_s, C, M, N, K, out_dtype);
+  if (st != FBG_SUCCESS) return st;
+  if (variant < FBG_VARIANT_AUTO || variant > FBG_VARIANT_SWAP_AB_SPLITK || split_k < 0)
+    return FBG_ERROR_INVALID_VALUE;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (M == 0 || N == 0) return FBG_SUCCESS;
+  if (K == 0) {
+    // Still honour a forced variant's guard before filling.
+    fbg_plan p;
+    st = fbg::make_plan(M, N, K, out_dtype, 256, variant, split_k, &p, -1);
+    if (st != FBG_SUCCESS) return st;
+    return fbg::launch_fill_zero(C, M * N, out_dtype, stream) == hipSuccess ? FBG_SUCCESS : FBG_ERROR_HIP;
+  }
+  const int cu = device_cu_count(&st);
+  if (st != FBG_SUCCESS) return st;
+  fbg_plan p;
+  st = fbg::make_plan(M, N, K, out_dtype, cu, variant, split_k, &p, forced_config());
+  if (st != FBG_SUCCESS) return st;
+
+  fbg::GemmArgs args;
+  args.A = static_cast<const uint8_t*>(A);
+  args.a_s = a_s;
+  args.B = static_cast<const uint8_t*>(B);
+  args.b_s = b_s;
+  args.C = C;
+  args.M = (int)M;
+  args.N = (int)N;
+  args.K = (int)K;
+  args.out = out_dtype;
+  args.vec = (N % 4 == 0) && aligned(C, (uintptr_t)(4 * elem_size(out_dtype)));
+  args.stream = stream;
+
+  if (env_flag("FBG_LOG"))
+    fprintf(stderr, "fp8bg: M=%lld N=%lld K=%lld out=%d -> variant=%d cfg=%d tile=%dx%d S=%d grid=%lld ws=%lld\n",
+            (long long)M, (long long)N, (long long)K, out_dtype, p.variant, p.config, p.tile_m, p.tile_n, p.split_k,
+            (long long)p.grid, (long long)p.workspace_bytes);
+
+  if (p.workspace_bytes == 0) return launch_plan(p, args, nullptr, M, N);
+
+  if (workspace) {
+    if (workspace_size < (size_t)p.workspace_bytes) return FBG_ERROR_OUT_OF_MEMORY;
+    if (!aligned(workspace, 16)) return FBG_ERROR_UNSUPPORTED;
+    return launch_plan(p, args, workspace, M, N);
+  }
+  // Library-owned workspace: stream-ordered, so concurrent streams never share one.
+  if (env_flag("FBG_TEST_FAIL_ALLOC")) return FBG_ERROR_OUT_OF_MEMORY;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, (size_t)p.workspace_bytes, stream) != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return FBG_ERROR_OUT_OF_MEMORY;
+  }
+  const int64_t coff = fbg::workspace_counter_offset(p, M, N);
+  if (hipMemsetAsync(static_cast<char*>(ws) + coff, 0, (size_t)(p.workspace_bytes - coff), stream) != hipSuccess) {
+    (void)hipFreeAsync(ws, stream);
+    return FBG_ERROR_HIP;
+  }
+  st = launch_plan(p, args, ws, M, N);
+  if (hipFreeAsync(ws, stream) != hipSuccess && st == FBG_SUCCESS) st = FBG_ERROR_HIP;
+  return st;
+}
+
+extern "C" int fp8_block_gemm(const void* A, const float* a_s, const void* B, const float* b_s, void* C, int64_t M,
+                              int64_t N, int64_t K, int out_dtype, void* stream) {
+  return fp8_block_gemm_ex(A, a_s, B, b_s, C, M, N, K, out_dtype, stream, FBG_VARIANT_AUTO, 0, nullptr, 0);
+}
+
+extern "C" size_t fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int variant, int split_k) {
+  int cu = 256;
+  if (variant == FBG_VARIANT_AUTO || split_k == 0) {
+    int st = FBG_SUCCESS;
+    cu = device_cu_count(&st);
+    if (st != FBG_SUCCESS) return (size_t)-1;
+  }
+  fbg_plan p;
+  if (fbg::make_plan(M, N, K, FBG_OUT_BF16, cu, variant, split_k, &p, forced_config()) != FBG_SUCCESS)
+    return (size_t)-1;
+  return (size_t)p.workspace_bytes;
+}

@@ -1,0 +1,84 @@
+// Kernel configurations of each variant.  One X-macro list per variant feeds
+// both the host planner's table (which chooses a configuration) and the
+// launchers' switch (which maps it to a template instance), so the two
+// cannot disagree on a tile shape.  Plain host/device-neutral C++.
+#pragma once
+
+namespace fbg {
+
+// Generic LDS-staged kernel: id, block tile BM x BN, waves WAVES_M x WAVES_N.
+#define FBG_GENERIC_CFGS(X) \
+  X(0, 128, 128, 2, 2)      \
+  X(1, 256, 128, 2, 2)      \
+  X(2, 64, 128, 1, 2)
+
+// Skinny kernels (swap-AB and its split-K form): id, NB16 16-row blocks of
+// weight rows (output columns n), MB16 16-column blocks of activation rows
+// (output rows m), KW waves splitting the workgroup's K range, GPW groups
+// per wave per chunk.
+#define FBG_SWAP_CFGS(X) \
+  X(0, 1, 4, 4, 1)       \
+  X(1, 1, 4, 1, 2)       \
+  X(2, 1, 1, 4, 1)       \
+  X(3, 1, 2, 4, 1)       \
+  X(4, 2, 4, 2, 1)       \
+  X(5, 1, 8, 4, 1)       \
+  X(6, 4, 1, 4, 1)       \
+  X(7, 2, 1, 4, 1)       \
+  X(8, 1, 4, 2, 2)       \
+  X(9, 2, 2, 4, 1)       \
+  X(10, 1, 1, 16, 2)     \
+  X(11, 1, 1, 8, 2)      \
+  X(12, 2, 8, 8, 1)      \
+  X(13, 1, 8, 8, 1)      \
+  X(14, 1, 4, 8, 1)      \
+  X(15, 1, 2, 8, 2)      \
+  X(16, 2, 1, 8, 1)      \
+  X(17, 4, 1, 8, 1)      \
+  X(18, 1, 4, 4, 2)      \
+  X(19, 2, 4, 4, 1)      \
+  X(20, 1, 1, 4, 4)      \
+  X(21, 2, 1, 4, 2)
+
+// Short-K (K == 256, two groups, fully unrolled): same fields, KW * GPW == 2.
+#define FBG_SHORT_CFGS(X) \
+  X(0, 1, 4, 1, 2)        \
+  X(1, 2, 4, 1, 2)        \
+  X(2, 1, 1, 1, 2)        \
+  X(3, 1, 2, 1, 2)        \
+  X(4, 4, 1, 1, 2)        \
+  X(5, 1, 4, 2, 1)        \
+  X(6, 2, 2, 1, 2)        \
+  X(7, 1, 8, 2, 1)        \
+  X(8, 2, 12, 2, 1)       \
+  X(9, 1, 12, 2, 1)       \
+  X(10, 2, 4, 2, 1)       \
+  X(11, 4, 4, 2, 1)
+
+struct GenericCfg { int bm, bn, waves_m, waves_n; };
+constexpr GenericCfg kGenericCfgs[] = {
+#define X(id, bm, bn, wm, wn) {bm, bn, wm, wn},
+    FBG_GENERIC_CFGS(X)
+#undef X
+};
+constexpr int kNumGenericCfgs = sizeof(kGenericCfgs) / sizeof(kGenericCfgs[0]);
+
+struct SkinnyCfg { int nb16, mb16, kw, gpw; };
+constexpr SkinnyCfg kSwapCfgs[] = {
+#define X(id, nb, mb, kw, gpw) {nb, mb, kw, gpw},
+    FBG_SWAP_CFGS(X)
+#undef X
+};
+constexpr int kNumSwapCfgs = sizeof(kSwapCfgs) / sizeof(kSwapCfgs[0]);
+
+constexpr SkinnyCfg kShortCfgs[] = {
+#define X(id, nb, mb, kw, gpw) {nb, mb, kw, gpw},
+    FBG_SHORT_CFGS(X)
+#undef X
+};
+constexpr int kNumShortCfgs = sizeof(kShortCfgs) / sizeof(kShortCfgs[0]);
+
+inline int skinny_tile_n(const SkinnyCfg& c) { return 16 * c.nb16; }
+inline int skinny_tile_m(const SkinnyCfg& c) { return 16 * c.mb16; }
+
+}  // namespace fbg

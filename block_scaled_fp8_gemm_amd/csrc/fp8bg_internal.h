@@ -1,0 +1,43 @@
+// Internal interfaces between the C-ABI layer, the planner and the kernel
+// launchers.  Not installed; the public interface is include/fp8bg.h.
+#pragma once
+
+#include <stdint.h>
+
+#include "fp8bg.h"
+
+#ifdef __HIPCC__
+#include <hip/hip_runtime.h>
+#endif
+
+namespace fbg {
+
+// Planner (pure host code, fp8bg_plan.cpp).  Fills *out for a validated shape.
+// force_cfg >= 0 overrides the tile configuration within the chosen variant.
+int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int variant, int split_k,
+              fbg_plan* out, int force_cfg);
+
+// Bytes of split-K workspace for a plan: FP32 partials, then one counter per tile.
+int64_t workspace_bytes(const fbg_plan& p, int64_t M, int64_t N);
+int64_t workspace_counter_offset(const fbg_plan& p, int64_t M, int64_t N);
+
+#ifdef __HIPCC__
+struct GemmArgs {
+  const uint8_t* A;
+  const float* a_s;
+  const uint8_t* B;
+  const float* b_s;
+  void* C;
+  int M, N, K;
+  int out;
+  int vec;  // N % 4 == 0 and C aligned for 4-element vector stores
+  hipStream_t stream;
+};
+
+hipError_t launch_generic(const GemmArgs& a, int cfg, int64_t grid, int band);
+hipError_t launch_swap(const GemmArgs& a, int cfg, int64_t grid, int S, float* ws, unsigned* counters);
+hipError_t launch_short_k256(const GemmArgs& a, int cfg, int64_t grid);
+hipError_t launch_fill_zero(void* C, int64_t count, int out, hipStream_t stream);
+#endif
+
+}  // namespace fbg

@@ -1,0 +1,469 @@
+// gfx950 kernels of the block-scaled FP8 GEMM and their launchers.
+//
+//   C[m,n] = sum_g a_s[m,g] * b_s[n/128,g] * sum_{k in g} A[m,k] * B[n,k]
+//
+// (FlagGems-vllm PR #693, "feat: optimize w8a8 block fp8 matmul for Hopper",
+// sections "Description" and "Specialized kernels and the optimization
+// idea".)  The pages' kernels were Hopper/Triton designs; these are written
+// for CDNA4: 64-lane waves, the 16x16x128 FP8 MFMA (one MFMA consumes exactly
+// one 128-wide scale group, so its output is the group's fresh partial),
+// swizzled LDS tiles, and XCD-aware workgroup placement.
+//
+// Every kernel computes, per output element, the same FP32 chain
+//   acc = 0; for g in its group range: acc = fma(P_g, a_s[m,g] * b_s[n/128,g], acc)
+// and casts once (round to nearest even).
+#include "fp8bg_device.hpp"
+#include "fp8bg_configs.h"
+#include "fp8bg_internal.h"
+
+namespace fbg {
+
+// ===========================================================================
+// Generic kernel: LDS-staged A and B tiles, two stages, one group per step.
+// (The pages' generic tuned GEMM and its GROUP_M raster, section
+// "Specialized kernels and the optimization idea".)
+// ===========================================================================
+template <int BM, int BN, int WAVES_M, int WAVES_N, int OUT>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_generic(
+    const uint8_t* __restrict__ A, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
+    const float* __restrict__ b_s, void* __restrict__ C, int M, int N, int K, int band) {
+  constexpr int NT = 64 * WAVES_M * WAVES_N;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int IB = WM / 16, JB = WN / 16;
+  constexpr int A_PER_T = BM * 8 / NT, B_PER_T = BN * 8 / NT;
+  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile slots must split evenly over threads");
+  static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one b_s block");
+  static_assert(BM <= NT, "one a_s value per thread");
+
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * 128];
+  __shared__ __attribute__((aligned(16))) float sAs[2][BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int G = K / kGroup;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  raster(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, band, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nblk = (N + 127) / 128;
+  int nb = (n0 + wn * WN) >> 7;
+  nb = nb < nblk ? nb : nblk - 1;
+
+  const uint8_t* pa[A_PER_T];
+  const uint8_t* pb[B_PER_T];
+#pragma unroll
+  for (int i = 0; i < A_PER_T; ++i) pa[i] = slot_src(A, K, m0, M, tid + i * NT, 0);
+#pragma unroll
+  for (int i = 0; i < B_PER_T; ++i) pb[i] = slot_src(B, K, n0, N, tid + i * NT, 0);
+  const int arow = (m0 + tid) < M ? (m0 + tid) : (M - 1);
+  const float* pas = a_s + (int64_t)arow * G;
+
+  v4i ra[A_PER_T], rb[B_PER_T];
+  float ras = 0.f;
+  auto gload = [&](int g) {
+    const int k0 = g * kGroup;
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const v4i*>(pa[i] + k0);
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) rb[i] = *reinterpret_cast<const v4i*>(pb[i] + k0);
+    if (tid < BM) ras = pas[g];
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) *reinterpret_cast<v4i*>(sA[st] + 16 * (tid + i * NT)) = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) *reinterpret_cast<v4i*>(sB[st] + 16 * (tid + i * NT)) = rb[i];
+    if (tid < BM) sAs[st][tid] = ras;
+  };
+
+  v4f acc[IB][JB];
+#pragma unroll
+  for (int i = 0; i < IB; ++i)
+#pragma unroll
+    for (int j = 0; j < JB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (G > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int g = 0; g < G; ++g) {
+    const int cur = g & 1;
+    if (g + 1 < G) gload(g + 1);
+    const float bsv = b_s[(int64_t)nb * G + g];
+    float s[IB][4];
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+      const v4f a4 = *reinterpret_cast<const v4f*>(&sAs[cur][wm * WM + 16 * i + 4 * (lane >> 4)]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[i][r] = a4[r] * bsv;
+    }
+    v8i bf[JB];
+#pragma unroll
+    for (int j = 0; j < JB; ++j) bf[j] = load_frag_lds(sB[cur], wn * WN + 16 * j, lane);
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+      const v8i af = load_frag_lds(sA[cur], wm * WM + 16 * i, lane);
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        const v4f p = mfma_group(af, bf[j]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], s[i][r], acc[i][j][r]);
+      }
+    }
+    if (g + 1 < G) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // P[i][j] = sum A[m_i] B[n_j]: lane holds m = 4*(lane>>4)+r, n = lane & 15 of each block.
+#pragma unroll
+  for (int i = 0; i < IB; ++i)
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      const int n = n0 + wn * WN + 16 * j + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * WM + 16 * i + 4 * (lane >> 4) + r;
+        if (m < M && n < N) store1<OUT>(C, (int64_t)m * N + n, acc[i][j][r]);
+      }
+    }
+}
+
+// ===========================================================================
+// Skinny kernel: swap-AB, optionally split over K, and (KFIX = 2) the
+// short-K kernel.  (Section "Specialized kernels and the optimization idea":
+// swap_ab, swap_ab_splitk, short_k256.)
+//
+// Computes tiles of C^T = B A^T: weight rows n sit on the MFMA's first
+// operand, activation rows m (small M) on the second, so each lane ends with
+// 4 consecutive n of one output row m -- one vector store per block.
+//
+// Small-M shapes are latency- and bandwidth-bound, so operands are not staged
+// through LDS: every wave loads its own B and A fragments straight from
+// global memory into registers, all loads of a chunk of GPW groups in flight
+// at once and the next chunk prefetched while the current one is computed.
+// The KW waves of a workgroup split the workgroup's K range (wave kw takes
+// chunks kw, kw+KW, ...); their FP32 partials are summed through LDS in the
+// fixed order kw = 0..KW-1.
+//
+// Split-K over workgroups (S > 1): workgroup (tile, s) covers groups
+// [s*G/S, (s+1)*G/S) and publishes its FP32 partial at device scope; the last
+// of the S workgroups of a tile to arrive (one counter atomic per workgroup,
+// no atomics on data) sums the S partials in the fixed order s = 0..S-1,
+// casts, stores and resets the counter.  The page's split-K summed partials
+// with atomic adds into C (section "Numerical safety"), which is not
+// bit-reproducible; this order is.
+//
+// KFIX = 2 (short-K, K == 256): the group count is a compile-time 2, so the
+// loads and the fold are fully unrolled; each lane forms a_s*b_s of both
+// groups once per tile (b_s folded into a_s) and the two partials combine as
+// fma(P1, s1, fma(P0, s0, 0)).
+// ===========================================================================
+template <int NB16, int MB16, int KW, int GPW, int KFIX, int OUT>
+__global__ __launch_bounds__(64 * KW) void k_skinny(
+    const uint8_t* __restrict__ A, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
+    const float* __restrict__ b_s, void* __restrict__ C, int M, int N, int K, int S,
+    float* __restrict__ ws, unsigned* __restrict__ counters, int vec_ok) {
+  constexpr int BN = 16 * NB16;   // n rows per workgroup (every wave covers all of them)
+  constexpr int BMS = 16 * MB16;  // m columns per workgroup
+  constexpr int NBLK = NB16 * MB16;
+  static_assert(128 % BN == 0, "a tile's n rows must share one b_s block");
+  static_assert(KFIX == 0 || KW * GPW == KFIX, "the short-K form covers its groups in one chunk");
+
+  __shared__ __attribute__((aligned(16))) float sRed[KW > 1 ? KW : 1][NBLK][4][64];
+  __shared__ int sLast;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int kw = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = KFIX ? KFIX : K / kGroup;
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BMS - 1) / BMS;
+  const int T = tiles_n * tiles_m;
+  const int lid = xcd_remap(blockIdx.x, T * S);
+  const int s = lid / T, tile = lid - s * T;
+  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+  const int m0 = tm * BMS, n0 = tn * BN;
+  const int g_lo = (int)((int64_t)s * G / S), g_hi = (int)((int64_t)(s + 1) * G / S);
+  const int nblk = (N + 127) / 128;
+  const int nb = (n0 >> 7) < nblk ? (n0 >> 7) : nblk - 1;
+  const int64_t ldk = KFIX ? (int64_t)KFIX * kGroup : (int64_t)K;
+
+  // Row pointers (clamped rows only feed outputs that are never stored).
+  const uint8_t* pb[NB16];
+#pragma unroll
+  for (int i = 0; i < NB16; ++i) {
+    const int r = n0 + 16 * i + (lane & 15);
+    pb[i] = B + (int64_t)(r < N ? r : N - 1) * ldk;
+  }
+  const uint8_t* pa[MB16];
+  const float* pas[MB16];
+#pragma unroll
+  for (int j = 0; j < MB16; ++j) {
+    int r = m0 + 16 * j + (lane & 15);
+    r = r < M ? r : M - 1;
+    pa[j] = A + (int64_t)r * ldk;
+    pas[j] = a_s + (int64_t)r * G;
+  }
+  const float* pbs = b_s + (int64_t)nb * G;
+
+  struct Chunk {
+    v8i bf[GPW][NB16];
+    v8i af[GPW][MB16];
+    float as[GPW][MB16];
+    float bs[GPW];
+  };
+  // Chunk c of this wave: groups g_lo + (c*KW + kw)*GPW + u, u < GPW.  Only
+  // chunks with at least one group in range are loaded; inside the last one,
+  // groups past the range are clamped (never computed).  Loads carry no
+  // per-group condition, so the compiler counts outstanding loads exactly
+  // and waits only for the chunk about to be used.
+  auto load = [&](Chunk& ch, int c) {
+    const int g0 = g_lo + (c * KW + kw) * GPW;
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      const int g = (g0 + u) < g_hi ? (g0 + u) : (g_hi - 1);
+      const int k0 = g * kGroup;
+#pragma unroll
+      for (int i = 0; i < NB16; ++i) ch.bf[u][i] = load_frag_global(pb[i] + k0, lane);
+#pragma unroll
+      for (int j = 0; j < MB16; ++j) ch.af[u][j] = load_frag_global(pa[j] + k0, lane);
+#pragma unroll
+      for (int j = 0; j < MB16; ++j) ch.as[u][j] = pas[j][g];
+      ch.bs[u] = pbs[g];
+    }
+  };
+
+  v4f acc[NB16][MB16];
+#pragma unroll
+  for (int i = 0; i < NB16; ++i)
+#pragma unroll
+    for (int j = 0; j < MB16; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Chunk& ch, int c) {
+    const int g0 = g_lo + (c * KW + kw) * GPW;
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      if (g0 + u < g_hi) {
+#pragma unroll
+        for (int j = 0; j < MB16; ++j) {
+          const float sc = ch.as[u][j] * ch.bs[u];  // a_s * b_s, once per group and lane
+#pragma unroll
+          for (int i = 0; i < NB16; ++i) {
+            const v4f p = mfma_group(ch.bf[u][i], ch.af[u][j]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], sc, acc[i][j][r]);
+          }
+        }
+      }
+    }
+  };
+
+  // Chunks of this wave that hold at least one group of [g_lo, g_hi).
+  const int first = g_lo + kw * GPW;
+  const int my_chunks = first < g_hi ? (g_hi - first + KW * GPW - 1) / (KW * GPW) : 0;
+  if constexpr (KFIX != 0) {
+    if (my_chunks > 0) {
+      Chunk ch;
+      load(ch, 0);
+      compute(ch, 0);
+    }
+  } else if (my_chunks > 0) {
+    // Two register buffers in ping-pong, no copies between them: chunk c+1
+    // is in flight while chunk c is computed.  The steady-state loop runs
+    // while two more chunks exist; the last one or two are peeled.
+    Chunk b0, b1;
+    load(b0, 0);
+    int c = 0;
+    for (; c + 2 < my_chunks; c += 2) {
+      load(b1, c + 1);
+      compute(b0, c);
+      load(b0, c + 2);
+      compute(b1, c + 1);
+    }
+    if (my_chunks - c == 2) {
+      load(b1, c + 1);
+      compute(b0, c);
+      compute(b1, c + 1);
+    } else {
+      compute(b0, c);
+    }
+  }
+
+  // Sum the KW waves' partials in the fixed order kw = 0..KW-1; wave w then
+  // owns blocks b with b % KW == w for the rest of the epilogue.
+  if constexpr (KW > 1) {
+#pragma unroll
+    for (int i = 0; i < NB16; ++i)
+#pragma unroll
+      for (int j = 0; j < MB16; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sRed[kw][i * MB16 + j][r][lane] = acc[i][j][r];
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      if (b % KW != kw) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = sRed[0][b][r][lane];
+#pragma unroll
+        for (int q = 1; q < KW; ++q) v += sRed[q][b][r][lane];
+        acc[b / MB16][b % MB16][r] = v;
+      }
+    }
+  }
+
+  if (S > 1) {
+    // Publish this split's partial at device scope: agent-scope stores are
+    // written through the XCD's L2 to the device coherence point, so the
+    // reducing workgroup (maybe on another XCD) reads them without a
+    // whole-L2 writeback or invalidate.  Order: every store complete
+    // (s_waitcnt) -> barrier -> one arrival increment per workgroup.
+    constexpr int TILE_ELEMS = BN * BMS;
+    float* mine = ws + ((int64_t)s * T + tile) * TILE_ELEMS;
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      if (b % KW != kw) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        __hip_atomic_store(mine + (b * 4 + r) * 64 + lane, acc[b / MB16][b % MB16][r], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sLast = (prev == (unsigned)(S - 1));
+    }
+    __syncthreads();
+    if (!sLast) return;
+    // Last arrival: sum the S partials in the fixed order q = 0..S-1, all
+    // loads of one split issued before its adds.
+    const float* wt = ws + (int64_t)tile * TILE_ELEMS;
+    const int64_t split_stride = (int64_t)T * TILE_ELEMS;
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      if (b % KW != kw) continue;
+      v4f v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        v[r] = __hip_atomic_load(wt + (b * 4 + r) * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int q = 1; q < S; ++q) {
+        v4f t;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          t[r] = __hip_atomic_load(wt + q * split_stride + (b * 4 + r) * 64 + lane, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += t[r];
+      }
+      acc[b / MB16][b % MB16] = v;
+    }
+    if (tid == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // Result block (i, j): lane holds n = 16i + 4*(lane>>4) + r, m = 16j + (lane & 15).
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) {
+    if (b % KW != kw) continue;
+    const int i = b / MB16, j = b % MB16;
+    const int n = n0 + 16 * i + 4 * (lane >> 4);
+    const int m = m0 + 16 * j + (lane & 15);
+    const int cnt = N - n < 4 ? N - n : 4;
+    if (m < M && cnt > 0) store4<OUT>(C, (int64_t)m * N + n, acc[i][j], cnt, vec_ok);
+  }
+}
+
+// ===========================================================================
+// K == 0: the empty sum, C = +0.
+// ===========================================================================
+template <int OUT>
+__global__ void k_fill_zero(void* __restrict__ C, int64_t count) {
+  typedef typename Out<OUT>::T T;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
+    reinterpret_cast<T*>(C)[i] = Out<OUT>::cvt(0.f);
+}
+
+// ===========================================================================
+// Launchers
+// ===========================================================================
+template <int BM, int BN, int WM_, int WN_>
+static hipError_t launch_generic_t(const GemmArgs& a, int64_t grid, int band) {
+  const dim3 blk(64 * WM_ * WN_);
+  switch (a.out) {
+    case kOutBF16:
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, kOutBF16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
+                         a.b_s, a.C, a.M, a.N, a.K, band);
+      break;
+    case kOutFP16:
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, kOutFP16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
+                         a.b_s, a.C, a.M, a.N, a.K, band);
+      break;
+    default:
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, kOutFP32>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
+                         a.b_s, a.C, a.M, a.N, a.K, band);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_generic(const GemmArgs& a, int cfg, int64_t grid, int band) {
+  switch (cfg) {
+#define X(id, bm, bn, wm, wn) \
+  case id: return launch_generic_t<bm, bn, wm, wn>(a, grid, band);
+    FBG_GENERIC_CFGS(X)
+#undef X
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int NB16, int MB16, int KW, int GPW, int KFIX>
+static hipError_t launch_skinny_t(const GemmArgs& a, int64_t grid, int S, float* ws, unsigned* cnt) {
+  const dim3 blk(64 * KW);
+  switch (a.out) {
+    case kOutBF16:
+      hipLaunchKernelGGL((k_skinny<NB16, MB16, KW, GPW, KFIX, kOutBF16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+                         a.B, a.b_s, a.C, a.M, a.N, a.K, S, ws, cnt, a.vec);
+      break;
+    case kOutFP16:
+      hipLaunchKernelGGL((k_skinny<NB16, MB16, KW, GPW, KFIX, kOutFP16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+                         a.B, a.b_s, a.C, a.M, a.N, a.K, S, ws, cnt, a.vec);
+      break;
+    default:
+      hipLaunchKernelGGL((k_skinny<NB16, MB16, KW, GPW, KFIX, kOutFP32>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+                         a.B, a.b_s, a.C, a.M, a.N, a.K, S, ws, cnt, a.vec);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_swap(const GemmArgs& a, int cfg, int64_t grid, int S, float* ws, unsigned* counters) {
+  switch (cfg) {
+#define X(id, nb, mb, kw, gpw) \
+  case id: return launch_skinny_t<nb, mb, kw, gpw, 0>(a, grid, S, ws, counters);
+    FBG_SWAP_CFGS(X)
+#undef X
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_short_k256(const GemmArgs& a, int cfg, int64_t grid) {
+  switch (cfg) {
+#define X(id, nb, mb, kw, gpw) \
+  case id: return launch_skinny_t<nb, mb, kw, gpw, 2>(a, grid, 1, nullptr, nullptr);
+    FBG_SHORT_CFGS(X)
+#undef X
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fill_zero(void* C, int64_t count, int out, hipStream_t stream) {
+  const int64_t blocks64 = (count + 255) / 256;
+  const unsigned blocks = (unsigned)(blocks64 < 4096 ? (blocks64 > 0 ? blocks64 : 1) : 4096);
+  switch (out) {
+    case kOutBF16: hipLaunchKernelGGL(k_fill_zero<kOutBF16>, dim3(blocks), dim3(256), 0, stream, C, count); break;
+    case kOutFP16: hipLaunchKernelGGL(k_fill_zero<kOutFP16>, dim3(blocks), dim3(256), 0, stream, C, count); break;
+    default: hipLaunchKernelGGL(k_fill_zero<kOutFP32>, dim3(blocks), dim3(256), 0, stream, C, count);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fbg

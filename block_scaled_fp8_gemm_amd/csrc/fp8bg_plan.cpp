@@ -1,0 +1,179 @@
+// The (M, N, K) dispatcher: pure host code, no HIP calls, so it runs and is
+// tested without a GPU.
+//
+// The pages' dispatch routes each shape by (M, N, K) to the best-fit kernel,
+// every special path behind its own shape guard, with the generic kernel as
+// the fallback for everything else (FlagGems-vllm PR #693, "feat: optimize
+// w8a8 block fp8 matmul for Hopper", sections "Description" and "Numerical
+// safety").  The per-shape meta-parameters the pages tune offline (block
+// sizes, warps, stages, split-K; section "Specialized kernels and the
+// optimization idea") become, here, a configuration index and a split count
+// chosen from the shape and the device's compute-unit count.
+#include <limits.h>
+#include <string.h>
+
+#include "fp8bg.h"
+#include "fp8bg_configs.h"
+#include "fp8bg_internal.h"
+
+namespace fbg {
+
+namespace {
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t skinny_tiles(const SkinnyCfg& c, int64_t M, int64_t N) {
+  return cdiv(N, skinny_tile_n(c)) * cdiv(M, skinny_tile_m(c));
+}
+
+// Activation-tile width (16-column blocks) of the skinny family: cover all of
+// M in one tile when M <= 128, so every weight row is streamed exactly once;
+// wider M is tiled in 64-column steps.
+int skinny_mb16_for(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : (M <= 128 ? 8 : 4))); }
+
+int swap_cfg_for(int64_t M) {
+  switch (skinny_mb16_for(M)) {
+    case 1: return 2;   // 16 n x 16 m, 4 waves split K
+    case 2: return 3;   // 16 n x 32 m
+    case 8: return 5;   // 16 n x 128 m
+    default: return 0;  // 16 n x 64 m
+  }
+}
+
+int short_cfg_for(int64_t M) {
+  switch (skinny_mb16_for(M)) {
+    case 1: return 2;   // 16 n x 16 m
+    case 2: return 3;   // 16 n x 32 m
+    case 8: return 7;   // 16 n x 128 m, 2 waves (one group each)
+    default: return 0;  // 16 n x 64 m
+  }
+}
+
+int generic_cfg_for(int64_t M, int64_t N, int cu) {
+  if (M <= 64) return 2;
+  const int64_t t256x128 = cdiv(M, 256) * cdiv(N, 128);
+  if (t256x128 >= 2 * (int64_t)cu) return 1;
+  return 0;
+}
+
+}  // namespace
+
+int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int variant, int split_k,
+              fbg_plan* out, int force_cfg) {
+  if (!out) return FBG_ERROR_INVALID_VALUE;
+  memset(out, 0, sizeof *out);
+  out->split_k = 1;
+  out->config = -1;
+  if (M < 0 || N < 0 || K < 0 || split_k < 0) return FBG_ERROR_INVALID_VALUE;
+  if (out_dtype != FBG_OUT_BF16 && out_dtype != FBG_OUT_FP16 && out_dtype != FBG_OUT_FP32)
+    return FBG_ERROR_INVALID_VALUE;
+  if (variant < FBG_VARIANT_AUTO || variant > FBG_VARIANT_SWAP_AB_SPLITK) return FBG_ERROR_INVALID_VALUE;
+  if (K % 128 != 0) return FBG_ERROR_UNSUPPORTED;
+  if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return FBG_ERROR_UNSUPPORTED;
+  const int cu = cu_count > 0 ? cu_count : 256;
+  const int64_t G = K / 128;
+
+  // Guards of forced variants: a forced path whose guard fails is an error,
+  // never a silent fallback.
+  if (variant == FBG_VARIANT_SHORT_K256 && K != 256) return FBG_ERROR_UNSUPPORTED;
+  if (split_k > 1 && variant != FBG_VARIANT_SWAP_AB_SPLITK) return FBG_ERROR_UNSUPPORTED;
+  if (split_k > G && G > 0) return FBG_ERROR_UNSUPPORTED;
+
+  if (M == 0 || N == 0 || K == 0) {  // nothing to multiply: no GEMM kernel
+    out->variant = variant;
+    return FBG_SUCCESS;
+  }
+
+  int v = variant;
+  if (v == FBG_VARIANT_AUTO) {
+    if (K == 256 && M <= 1024)
+      v = FBG_VARIANT_SHORT_K256;
+    else if (M <= 128)
+      v = FBG_VARIANT_SWAP_AB;  // may become split-K below
+    else
+      v = FBG_VARIANT_GENERIC;
+  }
+
+  out->variant = v;
+  if (force_cfg >= 0) {  // test / benchmark override of the tile configuration
+    const int n = v == FBG_VARIANT_GENERIC ? kNumGenericCfgs
+                                           : (v == FBG_VARIANT_SHORT_K256 ? kNumShortCfgs : kNumSwapCfgs);
+    if (force_cfg >= n) return FBG_ERROR_UNSUPPORTED;
+  }
+  if (v == FBG_VARIANT_GENERIC) {
+    const int c = force_cfg >= 0 ? force_cfg : generic_cfg_for(M, N, cu);
+    const GenericCfg& g = kGenericCfgs[c];
+    out->config = c;
+    out->tile_m = g.bm;
+    out->tile_n = g.bn;
+    out->waves = g.waves_m * g.waves_n;
+    out->grid = cdiv(M, g.bm) * cdiv(N, g.bn);
+  } else if (v == FBG_VARIANT_SHORT_K256) {
+    const int c = force_cfg >= 0 ? force_cfg : short_cfg_for(M);
+    const SkinnyCfg& k = kShortCfgs[c];
+    out->config = c;
+    out->tile_m = skinny_tile_m(k);
+    out->tile_n = skinny_tile_n(k);
+    out->waves = k.kw;
+    out->grid = skinny_tiles(k, M, N);
+  } else {  // SWAP_AB or SWAP_AB_SPLITK
+    const int c = force_cfg >= 0 ? force_cfg : swap_cfg_for(M);
+    const SkinnyCfg& k = kSwapCfgs[c];
+    const int64_t tiles = skinny_tiles(k, M, N);
+    int64_t S = 1;
+    if (split_k > 0) {
+      S = split_k;
+    } else if (variant == FBG_VARIANT_AUTO || variant == FBG_VARIANT_SWAP_AB_SPLITK) {
+      // Split K until the grid covers the device once, keeping at least one
+      // group per wave in every split.
+      const int64_t want = cdiv(cu, tiles);
+      const int64_t cap = G / k.kw > 1 ? G / k.kw : 1;
+      S = want < cap ? want : cap;
+      if (S < 1) S = 1;
+    }
+    if (variant == FBG_VARIANT_AUTO) v = S > 1 ? FBG_VARIANT_SWAP_AB_SPLITK : FBG_VARIANT_SWAP_AB;
+    out->variant = v;
+    out->config = c;
+    out->tile_m = skinny_tile_m(k);
+    out->tile_n = skinny_tile_n(k);
+    out->waves = k.kw;
+    out->split_k = (int32_t)S;
+    out->grid = tiles * S;
+  }
+  if (out->grid > INT_MAX) return FBG_ERROR_UNSUPPORTED;
+  out->workspace_bytes = workspace_bytes(*out, M, N);
+  return FBG_SUCCESS;
+}
+
+int64_t workspace_counter_offset(const fbg_plan& p, int64_t M, int64_t N) {
+  if (p.split_k <= 1 || p.tile_m <= 0 || p.tile_n <= 0) return 0;
+  const int64_t T = cdiv(M, p.tile_m) * cdiv(N, p.tile_n);
+  const int64_t partial = (int64_t)p.split_k * T * p.tile_m * p.tile_n * 4;
+  return cdiv(partial, 256) * 256;
+}
+
+int64_t workspace_bytes(const fbg_plan& p, int64_t M, int64_t N) {
+  if (p.split_k <= 1 || p.tile_m <= 0 || p.tile_n <= 0) return 0;
+  const int64_t T = cdiv(M, p.tile_m) * cdiv(N, p.tile_n);
+  return workspace_counter_offset(p, M, N) + T * 4;
+}
+
+}  // namespace fbg
+
+extern "C" int fp8_block_gemm_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int variant,
+                                   int split_k, fbg_plan* out) {
+  return fbg::make_plan(M, N, K, out_dtype, cu_count, variant, split_k, out, -1);
+}
+
+extern "C" const char* fp8_block_gemm_status_string(int status) {
+  switch (status) {
+    case FBG_SUCCESS: return "success";
+    case FBG_ERROR_INVALID_VALUE: return "invalid value (null pointer, negative size, bad dtype or overlapping output)";
+    case FBG_ERROR_UNSUPPORTED: return "unsupported (K % 128 != 0, misaligned pointer, or a forced variant's guard failed)";
+    case FBG_ERROR_OUT_OF_MEMORY: return "out of memory (split-K workspace unavailable or too small)";
+    case FBG_ERROR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int fp8_block_gemm_version(void) { return 100; }

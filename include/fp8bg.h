@@ -1,0 +1,142 @@
+/*
+ * fp8bg.h -- C ABI of the block-scaled FP8 GEMM library for AMD MI355X (gfx950).
+ *
+ * The operation (FlagGems-vllm PR #693, "feat: optimize w8a8 block fp8 matmul
+ * for Hopper", section "Description": FP8 E4M3 activations with per-token
+ * 1x128 scales, FP8 E4M3 weights with [block_n, block_k] = [128, 128] scales;
+ * section "Numerical safety": every path accumulates in FP32 and casts to the
+ * requested bf16 / fp16 / fp32 output):
+ *
+ *     C[m,n] = sum_g a_s[m,g] * b_s[n/128, g] * sum_{k = 128g}^{128g+127} A[m,k] * B[n,k]
+ *
+ * Layouts (all row-major, contiguous, no strides -- the same section's guard
+ * requires contiguous strides and group_k == 128):
+ *   A    [M, K]               OCP FP8 E4M3 bytes (torch.float8_e4m3fn)
+ *   a_s  [M, K/128]           fp32, per-token, per 128-wide K group
+ *   B    [N, K]               OCP FP8 E4M3 bytes (the weight W of y = x W^T)
+ *   b_s  [ceil(N/128), K/128] fp32, per 128x128 weight block
+ *   C    [M, N]               bf16 / fp16 / fp32 (out_dtype)
+ *
+ * Pointers are device pointers on the current HIP device unless a function
+ * says otherwise.  The caller owns every buffer; the library reads A, a_s, B,
+ * b_s, writes exactly C[0 .. M*N) and never reads C (no beta, no zero-fill
+ * requirement).  All calls are asynchronous on `stream` (a hipStream_t passed
+ * as void*, NULL = the null stream); device-side faults surface at the
+ * caller's next synchronisation.  No function throws or aborts.
+ *
+ * Numerics: each kernel forms the fresh FP32 partial of one 128-wide group on
+ * the MFMA units, then folds it as acc = fma(P, a_s*b_s, acc) in group order;
+ * the cast to the output dtype is round-to-nearest-even.  Every call is
+ * deterministic: the same inputs give the same bits on every run and stream.
+ */
+#ifndef FP8BG_H
+#define FP8BG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    FBG_SUCCESS = 0,
+    FBG_ERROR_INVALID_VALUE = 1,  /* null pointer, negative size, bad dtype, C overlapping an input */
+    FBG_ERROR_UNSUPPORTED = 2,    /* K % 128 != 0, misaligned pointer, a forced variant whose guard fails */
+    FBG_ERROR_OUT_OF_MEMORY = 3,  /* split-K workspace could not be allocated / is too small */
+    FBG_ERROR_HIP = 4             /* a HIP runtime call or kernel launch failed */
+};
+
+/* Output dtypes. */
+enum { FBG_OUT_BF16 = 0, FBG_OUT_FP16 = 1, FBG_OUT_FP32 = 2 };
+
+/* Kernel variants (the four specialised paths of the section "Specialized
+ * kernels and the optimization idea", re-designed for gfx950). */
+enum {
+    FBG_VARIANT_AUTO = 0,          /* the (M,N,K) dispatcher chooses */
+    FBG_VARIANT_GENERIC = 1,       /* LDS-staged MFMA tiles, any shape */
+    FBG_VARIANT_SHORT_K256 = 2,    /* K == 256: both groups unrolled, a_s*b_s pre-folded */
+    FBG_VARIANT_SWAP_AB = 3,       /* C^T = B A^T: weight rows on the 16-row MFMA side, small M on the other */
+    FBG_VARIANT_SWAP_AB_SPLITK = 4 /* swap-AB with K split over workgroups, fixed-order FP32 reduction */
+};
+
+/* One dispatcher decision (pure data, filled by fp8_block_gemm_plan). */
+typedef struct fbg_plan {
+    int32_t variant;      /* FBG_VARIANT_* actually used */
+    int32_t tile_m;       /* output rows (M) per workgroup */
+    int32_t tile_n;       /* output columns (N) per workgroup */
+    int32_t split_k;      /* number of K splits (1 = none) */
+    int32_t waves;        /* wavefronts (64 lanes) per workgroup */
+    int32_t config;       /* kernel configuration index within the variant */
+    int64_t grid;         /* workgroups launched */
+    int64_t workspace_bytes; /* device workspace the call needs (0 if none) */
+} fbg_plan;
+
+/*
+ * fp8_block_gemm -- C = block-scaled A * B^T, dispatcher-chosen kernel.
+ *
+ * M, N >= 0; K >= 0 with K % 128 == 0.  M == 0 or N == 0: success, nothing
+ * launched.  K == 0: C is filled with zeros (the empty sum).  A and B must be
+ * 16-byte aligned, a_s and b_s 4-byte aligned, C aligned to its element size.
+ * A null pointer with a non-empty extent, a negative size, an unknown
+ * out_dtype or a C range that overlaps an input range -> INVALID_VALUE;
+ * K % 128 != 0 or misalignment -> UNSUPPORTED.  When the chosen kernel splits
+ * K, its FP32 workspace is taken from a stream-ordered allocation on `stream`
+ * (hipMallocAsync / hipFreeAsync), so concurrent calls on different streams
+ * do not share it; failure -> OUT_OF_MEMORY before anything is launched.
+ */
+int fp8_block_gemm(const void *A, const float *a_s, const void *B, const float *b_s,
+                   void *C, int64_t M, int64_t N, int64_t K, int out_dtype, void *stream);
+
+/*
+ * fp8_block_gemm_ex -- the same operation with a forced variant and an
+ * explicit workspace (for tests, benchmarks and stream capture).
+ *
+ * variant: FBG_VARIANT_* (AUTO = as fp8_block_gemm).  A forced variant whose
+ * shape guard fails returns UNSUPPORTED; it never falls back silently.
+ * split_k: 0 = the dispatcher's choice, else the number of K splits (only
+ * SWAP_AB_SPLITK accepts > 1; it must not exceed K/128).
+ * workspace / workspace_bytes: caller-owned device memory of at least
+ * fp8_block_gemm_workspace_size(...) bytes, or NULL to let the library
+ * allocate it stream-ordered.  The workspace holds FP32 partials and one
+ * 32-bit arrival counter per output tile; the counters must be zero before
+ * the first call that uses the buffer, and every completed call leaves them
+ * zero again, so a buffer zeroed once can be reused by calls that are
+ * ordered on one stream.  Calls that overlap in time must not share one.
+ */
+int fp8_block_gemm_ex(const void *A, const float *a_s, const void *B, const float *b_s,
+                      void *C, int64_t M, int64_t N, int64_t K, int out_dtype, void *stream,
+                      int variant, int split_k, void *workspace, size_t workspace_bytes);
+
+/*
+ * fp8_block_gemm_workspace_size -- bytes of workspace fp8_block_gemm_ex needs
+ * for this shape, variant and split (0 when the chosen kernel needs none).
+ * variant / split_k as in fp8_block_gemm_ex; when either is left to the
+ * dispatcher the plan uses the current device's compute-unit count (one
+ * cached HIP query).  Returns (size_t)-1 for an invalid request.
+ */
+size_t fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int variant, int split_k);
+
+/*
+ * fp8_block_gemm_plan -- the dispatcher's decision for (M, N, K, out_dtype)
+ * on a device with cu_count compute units (the pages' dispatch routes each
+ * shape by (M, N, K) to the best-fit kernel, with the generic kernel as the
+ * fallback: section "Description").  Pure host code: makes no HIP call, so
+ * it can run without a GPU.  variant / split_k force a choice as in
+ * fp8_block_gemm_ex.  Returns SUCCESS and fills *out, or an error status.
+ */
+int fp8_block_gemm_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count,
+                        int variant, int split_k, fbg_plan *out);
+
+/* fp8_block_gemm_status_string -- static text for a status code. */
+const char *fp8_block_gemm_status_string(int status);
+
+/* fp8_block_gemm_version -- library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fp8_block_gemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BG_H */

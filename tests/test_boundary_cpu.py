@@ -1,0 +1,148 @@
+"""The C-ABI boundary without a GPU: the library loads and exports every
+function include/fp8bg.h declares; the dispatcher's plan (pure host code) and
+the host-side argument validation return the documented decisions and
+statuses.  No compute call is made (validation fails, or the shape is empty,
+before any HIP call).
+
+Dispatch contract (FlagGems-vllm PR #693, "feat: optimize w8a8 block fp8
+matmul for Hopper", sections "Description" and "Numerical safety"): each
+shape is routed by (M, N, K); each special path runs only under its guard;
+every other shape falls through to the generic kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_scaled_fp8_gemm_amd as fbg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bg.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fp8_block_gemm\w*)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fbg.load()
+    names = declared_functions()
+    assert len(names) >= 6, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.fp8_block_gemm_version() == 100
+
+
+def test_status_strings():
+    for st in range(5):
+        assert len(fbg.status_string(st)) > 3
+    assert fbg.status_string(99) == "unknown status"
+
+
+def test_plan_for_the_workloads():
+    p = fbg.plan(16, 512, 256)
+    assert p["variant_name"] == "short_k256" and p["split_k"] == 1
+    p = fbg.plan(64, 512, 4096)
+    assert p["variant_name"] == "swap_ab_splitk" and p["split_k"] > 1 and p["workspace_bytes"] > 0
+    assert p["grid"] >= 256
+    p = fbg.plan(184, 4096, 256)
+    assert p["variant_name"] == "short_k256"
+    p = fbg.plan(128, 8192, 1024)
+    assert p["variant_name"] in ("swap_ab", "swap_ab_splitk", "generic")
+    p = fbg.plan(16384, 4096, 4096)
+    assert p["variant_name"] == "generic" and p["workspace_bytes"] == 0
+
+
+@pytest.mark.parametrize("cu", [1, 8, 80, 256, 304, 1024])
+def test_plan_is_consistent_for_any_cu_count(cu):
+    for (M, N, K) in [(1, 4096, 1024), (64, 512, 4096), (300, 1000, 768), (16384, 4096, 4096), (7, 9, 128)]:
+        p = fbg.plan(M, N, K, cu_count=cu)
+        tiles = -(-M // p["tile_m"]) * -(-N // p["tile_n"])
+        assert p["grid"] == tiles * p["split_k"]
+        assert 1 <= p["split_k"] <= K // 128
+        if p["split_k"] > 1:
+            assert p["variant_name"] == "swap_ab_splitk"
+            assert p["workspace_bytes"] >= p["split_k"] * tiles * p["tile_m"] * p["tile_n"] * 4 + 4 * tiles
+        else:
+            assert p["workspace_bytes"] == 0
+
+
+def test_guard_fall_through_to_generic():
+    # outside every special guard (K != 256, M large): generic
+    for (M, N, K) in [(1025, 4096, 256), (129, 1024, 512), (5000, 300, 1152)]:
+        assert fbg.plan(M, N, K)["variant_name"] == "generic"
+
+
+def test_forced_variant_guards():
+    with pytest.raises(fbg.FP8BGError) as e:
+        fbg.plan(64, 512, 512, variant="short_k256")
+    assert e.value.status == fbg.UNSUPPORTED
+    with pytest.raises(fbg.FP8BGError) as e:
+        fbg.plan(64, 512, 512, variant="swap_ab", split_k=2)
+    assert e.value.status == fbg.UNSUPPORTED
+    with pytest.raises(fbg.FP8BGError) as e:
+        fbg.plan(64, 512, 512, variant="swap_ab_splitk", split_k=5)
+    assert e.value.status == fbg.UNSUPPORTED
+    with pytest.raises(fbg.FP8BGError) as e:
+        fbg.plan(64, 512, 200)
+    assert e.value.status == fbg.UNSUPPORTED
+    with pytest.raises(fbg.FP8BGError) as e:
+        fbg.plan(-1, 512, 256)
+    assert e.value.status == fbg.INVALID_VALUE
+    with pytest.raises(fbg.FP8BGError) as e:
+        fbg.plan(1, 512, 256, out_dtype=7)
+    assert e.value.status == fbg.INVALID_VALUE
+    p = fbg.plan(64, 512, 512, variant="swap_ab_splitk", split_k=1)
+    assert p["split_k"] == 1 and p["workspace_bytes"] == 0
+    assert fbg.plan(64, 512, 512, variant="generic")["variant_name"] == "generic"
+
+
+def test_workspace_size_for_forced_split():
+    n = fbg.workspace_size(64, 512, 4096, "swap_ab_splitk", 8)
+    p = fbg.plan(64, 512, 4096, variant="swap_ab_splitk", split_k=8)
+    assert n == p["workspace_bytes"] > 0
+    assert fbg.workspace_size(64, 512, 4096, "generic", 1) == 0
+
+
+def _call(A=0x10000, a_s=0x20000, B=0x30000, b_s=0x40000, C=0x50000000, M=16, N=256, K=256, out=0,
+          variant=0, split=0, ws=None, wsn=0):
+    lib = fbg.load()
+    return lib.fp8_block_gemm_ex(A, a_s, B, b_s, C, M, N, K, out, None, variant, split, ws, wsn)
+
+
+def test_host_validation_statuses():
+    # Pointers are never dereferenced here: validation fails (or the shape is
+    # empty) before any HIP call.
+    assert _call(A=None) == fbg.INVALID_VALUE
+    assert _call(a_s=None) == fbg.INVALID_VALUE
+    assert _call(B=None) == fbg.INVALID_VALUE
+    assert _call(b_s=None) == fbg.INVALID_VALUE
+    assert _call(C=None) == fbg.INVALID_VALUE
+    assert _call(M=-1) == fbg.INVALID_VALUE
+    assert _call(out=3) == fbg.INVALID_VALUE
+    assert _call(K=200) == fbg.UNSUPPORTED
+    assert _call(A=0x10008) == fbg.UNSUPPORTED              # A not 16-byte aligned
+    assert _call(B=0x30004) == fbg.UNSUPPORTED
+    assert _call(a_s=0x20002) == fbg.UNSUPPORTED
+    assert _call(C=0x50000001) == fbg.UNSUPPORTED           # bf16 C must be 2-byte aligned
+    assert _call(C=0x10000 + 64) == fbg.INVALID_VALUE       # C overlaps A
+    assert _call(C=0x40000) == fbg.INVALID_VALUE            # C overlaps b_s
+    assert _call(M=0, A=None, a_s=None, C=None) == fbg.SUCCESS   # empty: nothing launched
+    assert _call(N=0, B=None, b_s=None, C=None) == fbg.SUCCESS
+    assert _call(variant=9) == fbg.INVALID_VALUE
+    assert _call(split=-2) == fbg.INVALID_VALUE
+
+
+def test_python_wrapper_checks():
+    A = torch.zeros((4, 256), dtype=torch.float8_e4m3fn)
+    with pytest.raises(ValueError):
+        fbg.gemm(A, torch.zeros((4, 3)), torch.zeros((8, 256), dtype=torch.float8_e4m3fn), torch.zeros((1, 2)))
+    with pytest.raises(TypeError):
+        fbg.gemm(A.float(), torch.zeros((4, 2)), torch.zeros((8, 256), dtype=torch.float8_e4m3fn),
+                 torch.zeros((1, 2)))
+    with pytest.raises(ValueError):
+        fbg.gemm(A, torch.zeros((4, 2)), torch.zeros((8, 256), dtype=torch.float8_e4m3fn)[:, ::1].t(),
+                 torch.zeros((1, 2)))
