@@ -37,6 +37,36 @@ MALL_BYTES = 256 << 20
 METRIC = "TFLOP/s and % of roofline (HBM or FP8 MFMA) per (M,N,K), 1×MI355X"
 
 
+KERNEL_SOURCES = ["block_scaled_fp8_gemm_amd/csrc/fp8bg_kernels.hip", "block_scaled_fp8_gemm_amd/csrc/fp8bg_device.hpp",
+                  "block_scaled_fp8_gemm_amd/csrc/fp8bg_configs.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload, plan, out):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE profile
+    of this workload, if that profile was taken on the same kernel sources and
+    the same plan; else None."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic_record:"):
+            rec = json.loads(line.split(":", 1)[1])
+            same = (rec.get("source_hash") == kernel_source_hash() and rec.get("variant") == plan["variant_name"]
+                    and rec.get("config") == plan["config"] and rec.get("split_k") == plan["split_k"]
+                    and rec.get("out") == out)
+            return rec["traffic_bytes"] if same else None
+    return None
+
+
 def alg_bytes(M, N, K, out_bytes):
     """Each input read once, C written once (split-K partials are overhead)."""
     G, NB = K // 128, (N + 127) // 128
@@ -220,7 +250,7 @@ def main():
     r = run_workload(args, w, M, out, torch, fbg, W, args.steps, args.warmup, not args.no_graph,
                      args.variant, args.split, args.cfg)
     roof = dict(r["roof"])
-    roof["traffic"] = None
+    roof["traffic"] = profiled_traffic(w.name, r["plan"], out) if args.cfg is None else None
     line = {
         "metric": METRIC,
         "value": round(r["tflops"], 3),

@@ -26,28 +26,18 @@ int64_t skinny_tiles(const SkinnyCfg& c, int64_t M, int64_t N) {
   return cdiv(N, skinny_tile_n(c)) * cdiv(M, skinny_tile_m(c));
 }
 
-// Activation-tile width (16-column blocks) of the skinny family: cover all of
-// M in one tile when M <= 128, so every weight row is streamed exactly once;
-// wider M is tiled in 64-column steps.
-int skinny_mb16_for(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : (M <= 128 ? 8 : 4))); }
+// Tile configurations of the skinny family, from the configuration sweeps
+// of the decode, short-K and mid-M shapes (bench.py with forced variant,
+// split and configuration; every point kept in profiles/):
+//  - M <= 64: 16 n x 16 m tiles with 4 waves splitting K (swap-AB config 2);
+//    narrow tiles give the most workgroups, which beats streaming each
+//    weight row only once;
+//  - M <= 128: 32 n x 64 m tiles, 2 waves (config 4).
+int swap_cfg_for(int64_t M) { return M <= 64 ? 2 : 4; }
 
-int swap_cfg_for(int64_t M) {
-  switch (skinny_mb16_for(M)) {
-    case 1: return 2;   // 16 n x 16 m, 4 waves split K
-    case 2: return 3;   // 16 n x 32 m
-    case 8: return 5;   // 16 n x 128 m
-    default: return 0;  // 16 n x 64 m
-  }
-}
-
-int short_cfg_for(int64_t M) {
-  switch (skinny_mb16_for(M)) {
-    case 1: return 2;   // 16 n x 16 m
-    case 2: return 3;   // 16 n x 32 m
-    case 8: return 7;   // 16 n x 128 m, 2 waves (one group each)
-    default: return 0;  // 16 n x 64 m
-  }
-}
+// Short-K: 16 n x 16 m, one wave, both groups (config 2) up to M = 48;
+// above, 16 n x 64 m with 2 waves taking one group each (config 5).
+int short_cfg_for(int64_t M) { return M <= 48 ? 2 : 5; }
 
 int generic_cfg_for(int64_t M, int64_t N, int cu) {
   if (M <= 64) return 2;
