@@ -28,7 +28,7 @@ def hipcc() -> str:
 def flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-ffp-contract=off", "-Wall", "-Wno-unused-function",
+            "-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wall", "-Wno-unused-function",
             f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
@@ -54,6 +54,12 @@ def build(verbose: bool = False, jobs: int = 3) -> str:
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
+    # A kernel whose host launch stub was not emitted links fine into a
+    # shared library and only fails at load time: refuse it here.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", LIB + ".tmp"], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub" in l]
+    if missing:
+        raise RuntimeError(f"kernel launch stubs missing from the library: {missing[:3]}")
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -6,11 +6,13 @@
 
 namespace fbg {
 
-// Generic LDS-staged kernel: id, block tile BM x BN, waves WAVES_M x WAVES_N.
+// Generic LDS-staged kernel: id, block tile BM x BN, waves WAVES_M x WAVES_N,
+// LDS ring depth in groups.
 #define FBG_GENERIC_CFGS(X) \
-  X(0, 128, 128, 2, 2)      \
-  X(1, 256, 128, 2, 2)      \
-  X(2, 64, 128, 1, 2)
+  X(0, 128, 128, 2, 2, 4)   \
+  X(1, 256, 128, 2, 2, 3)   \
+  X(2, 64, 128, 1, 2, 4)    \
+  X(3, 256, 256, 2, 4, 2)
 
 // Skinny kernels (swap-AB and its split-K form): id, NB16 16-row blocks of
 // weight rows (output columns n), MB16 16-column blocks of activation rows
@@ -29,7 +31,7 @@ namespace fbg {
   X(9, 2, 2, 4, 1)       \
   X(10, 1, 1, 16, 2)     \
   X(11, 1, 1, 8, 2)      \
-  X(12, 2, 8, 8, 1)      \
+  X(12, 2, 8, 4, 1)      \
   X(13, 1, 8, 8, 1)      \
   X(14, 1, 4, 8, 1)      \
   X(15, 1, 2, 8, 2)      \
@@ -55,9 +57,9 @@ namespace fbg {
   X(10, 2, 4, 2, 1)       \
   X(11, 4, 4, 2, 1)
 
-struct GenericCfg { int bm, bn, waves_m, waves_n; };
+struct GenericCfg { int bm, bn, waves_m, waves_n, stages; };
 constexpr GenericCfg kGenericCfgs[] = {
-#define X(id, bm, bn, wm, wn) {bm, bn, wm, wn},
+#define X(id, bm, bn, wm, wn, st) {bm, bn, wm, wn, st},
     FBG_GENERIC_CFGS(X)
 #undef X
 };

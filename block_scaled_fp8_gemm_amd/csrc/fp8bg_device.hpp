@@ -1,6 +1,6 @@
 // Device building blocks shared by the gfx950 kernels of the block-scaled FP8
 // GEMM: the FP8 MFMA that forms one 128-wide group's partial, operand
-// fragments (from global memory or from swizzled LDS tiles), the per-group
+// fragments (from global memory or from fragment-major LDS tiles), the per-group
 // scale fold, and output conversion / stores.
 //
 // Operation (FlagGems-vllm PR #693, "feat: optimize w8a8 block fp8 matmul for
@@ -58,36 +58,22 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* row_ptr, int lane
 }
 
 // ---------------------------------------------------------------------------
-// LDS tiles: one group slice per row, 128 bytes = 8 chunks of 16 bytes.
-// Chunk c of row r is stored at slot 8r + (c ^ swz(r)).  swz is a bijection
-// on every 8 consecutive rows and keeps even and odd rows apart, so the 16
-// lanes that read chunk c of 16 consecutive rows touch 16 distinct 16-byte
-// bank groups (64 banks) and every 8 of them distinct groups (32 banks).
-// Writers fill slots linearly (thread t -> slot t), which is conflict-free,
-// and read global chunk (t & 7) ^ swz(t >> 3) of row t >> 3: 8 consecutive
-// threads cover one 128-byte row.
+// Fragment-major LDS tiles (generic kernel).  A 16-row block's group slice is
+// stored as two 1 KB images, one per half of the fragment (image x holds
+// bytes 64x .. 64x+63 of the group for the block's 16 rows): 16-byte slot
+// 4*r + c of image x holds row r, bytes 64x + 16c .. +16.  A fragment read
+// (lane l: row l & 15, slot c = l >> 4 of each image) touches every bank
+// group evenly, so ds_read_b128 runs without conflicts, and the
+// direct-to-LDS loads that fill an image (lane t -> slot t) read 64 contiguous
+// bytes per 4 adjacent lanes.  A row-major tile needs an XOR swizzle to keep
+// the 16 rows of a fragment read apart, and no swizzle measured on gfx950
+// read it conflict-free.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int r) { return (r + (r >> 3)) & 7; }
-
-__device__ __forceinline__ v8i load_frag_lds(const uint8_t* tile, int row0, int lane) {
-  const int r = row0 + (lane & 15);
-  const int h = lane >> 4;
-  const int s = swz(r);
-  const v4i lo = *reinterpret_cast<const v4i*>(tile + 128 * r + 16 * (h ^ s));
-  const v4i hi = *reinterpret_cast<const v4i*>(tile + 128 * r + 16 * ((h + 4) ^ s));
+__device__ __forceinline__ v8i load_frag_lds_fm(const uint8_t* tile, int block, int lane) {
+  const uint8_t* p = tile + block * 2048 + 64 * (lane & 15) + 16 * (lane >> 4);
+  const v4i lo = *reinterpret_cast<const v4i*>(p);
+  const v4i hi = *reinterpret_cast<const v4i*>(p + 1024);
   return join(lo, hi);
-}
-
-// Global source of LDS slot t of a tile whose rows start at global row `row0`
-// (rows at or past `rows` are clamped to the last valid row: they only feed
-// outputs that are never stored).
-__device__ __forceinline__ const uint8_t* slot_src(const uint8_t* X, int64_t ld, int row0, int rows,
-                                                   int t, int k0) {
-  const int r = t >> 3;
-  int gr = row0 + r;
-  gr = gr < rows ? gr : rows - 1;
-  const int c = (t & 7) ^ swz(r);
-  return X + (int64_t)gr * ld + k0 + 16 * c;
 }
 
 // ---------------------------------------------------------------------------
@@ -134,6 +120,30 @@ template <int OUT>
 __device__ __forceinline__ void store1(void* C, int64_t idx, float v) {
   reinterpret_cast<typename Out<OUT>::T*>(C)[idx] = Out<OUT>::cvt(v);
 }
+
+// Direct global -> LDS loads through a buffer resource: lane l's `size`
+// bytes, read at base + voff + soff, land at lds + l * size; `lds` and `soff`
+// are wave-uniform.  The resource spans 4 GiB from `base` with no stride;
+// callers keep every access inside its operand (rows are clamped), so the
+// range check never decides a result.  A tile base in SGPRs plus 32-bit
+// per-lane offsets replaces 64-bit per-lane addresses.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16(buf_rsrc r, uint32_t voff, int soff, lds_u8* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(buf_rsrc r, uint32_t voff, int soff, lds_u8* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, (int)voff, soff, 0, 0);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory loads of this
+// wave are outstanding and leaves the other counters alone (gfx9 layout:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_only(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 
 // ---------------------------------------------------------------------------
 // Workgroup -> tile mapping.  Workgroups are dispatched round-robin over the

@@ -7,7 +7,7 @@
 // idea".)  The pages' kernels were Hopper/Triton designs; these are written
 // for CDNA4: 64-lane waves, the 16x16x128 FP8 MFMA (one MFMA consumes exactly
 // one 128-wide scale group, so its output is the group's fresh partial),
-// swizzled LDS tiles, and XCD-aware workgroup placement.
+// fragment-major LDS tiles, and XCD-aware workgroup placement.
 //
 // Every kernel computes, per output element, the same FP32 chain
 //   acc = 0; for g in its group range: acc = fma(P_g, a_s[m,g] * b_s[n/128,g], acc)
@@ -19,27 +19,44 @@
 namespace fbg {
 
 // ===========================================================================
-// Generic kernel: LDS-staged A and B tiles, two stages, one group per step.
-// (The pages' generic tuned GEMM and its GROUP_M raster, section
-// "Specialized kernels and the optimization idea".)
+// Generic kernel: LDS-staged A and B tiles, STAGES-deep ring, one 128-wide
+// group per step.  (The pages' generic tuned GEMM and its GROUP_M raster,
+// section "Specialized kernels and the optimization idea".)
+//
+// Loads go straight from global memory into LDS (buffer_load_dwordx4 ... lds):
+// no staging registers and no LDS store instructions.  Every thread issues
+// the same LPG loads per group (A slots, B slots and one a_s load), so one
+// vmcnt bound per step says "this wave's loads of group g have landed"; a
+// barrier then makes the whole tile visible.  The loads of group g+STAGES-1
+// are issued once group g's tile is in LDS, into the slot every wave
+// finished reading in the previous step.
+//
+// Each MFMA writes a fresh FP32 partial; its fold acc = fma(P, s, acc) is
+// issued one block behind, in the shadow of the next MFMA (the schedule is
+// pinned with sched_group_barrier), so the VALU fold overlaps the MFMA pipe.
 // ===========================================================================
-template <int BM, int BN, int WAVES_M, int WAVES_N, int OUT>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_generic(
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int OUT>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
     const uint8_t* __restrict__ A, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
     const float* __restrict__ b_s, void* __restrict__ C, int M, int N, int K, int band) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;
+  constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int IB = WM / 16, JB = WN / 16;
   constexpr int A_PER_T = BM * 8 / NT, B_PER_T = BN * 8 / NT;
+  constexpr int LPG = A_PER_T + B_PER_T + 2;         // vector-memory loads per group per thread
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, S_BYTES = BM * 4 + 64 * 4;
+  constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
   static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile slots must split evenly over threads");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one b_s block");
-  static_assert(BM <= NT, "one a_s value per thread");
+  static_assert(BM >= 64 && BM % 64 == 0, "a_s rows are staged 64 per wave instruction");
+  static_assert(STAGES >= 2 && STAGES <= 4 && STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring must fit in 160 KB");
+  static_assert(2 * LPG < 64, "vmcnt counts at most 63 outstanding loads");
 
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * 128];
-  __shared__ __attribute__((aligned(16))) float sAs[2][BM];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[STAGES * STAGE_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int G = K / kGroup;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -47,34 +64,48 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_generic(
   raster(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, band, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int nblk = (N + 127) / 128;
-  int nb = (n0 + wn * WN) >> 7;
-  nb = nb < nblk ? nb : nblk - 1;
+  const int nb = ((n0 + wn * WN) >> 7) < nblk ? ((n0 + wn * WN) >> 7) : nblk - 1;
 
-  const uint8_t* pa[A_PER_T];
-  const uint8_t* pb[B_PER_T];
+  // Per-lane 32-bit source offsets inside the tile's rows (rows past the
+  // matrix are clamped to its last row: they feed outputs never stored).
+  // Load q (q = i*NW + wave) fills fragment-major image q: row block q >> 1,
+  // half q & 1; lane l supplies row 16*(q>>1) + (l >> 2), bytes
+  // 64*(q & 1) + 16*(l & 3).
+  const uint8_t* Atile = A + (int64_t)m0 * K;
+  const uint8_t* Btile = B + (int64_t)n0 * K;
+  uint32_t aoff[A_PER_T], boff[B_PER_T];
 #pragma unroll
-  for (int i = 0; i < A_PER_T; ++i) pa[i] = slot_src(A, K, m0, M, tid + i * NT, 0);
+  for (int i = 0; i < A_PER_T; ++i) {
+    const int q = i * NW + wave, r = 16 * (q >> 1) + (lane >> 2);
+    const int gr = (m0 + r) < M ? r : (M - 1 - m0);
+    aoff[i] = (uint32_t)gr * (uint32_t)K + 16u * (uint32_t)((lane & 3) + 4 * (q & 1));
+  }
 #pragma unroll
-  for (int i = 0; i < B_PER_T; ++i) pb[i] = slot_src(B, K, n0, N, tid + i * NT, 0);
-  const int arow = (m0 + tid) < M ? (m0 + tid) : (M - 1);
-  const float* pas = a_s + (int64_t)arow * G;
+  for (int i = 0; i < B_PER_T; ++i) {
+    const int q = i * NW + wave, r = 16 * (q >> 1) + (lane >> 2);
+    const int gr = (n0 + r) < N ? r : (N - 1 - n0);
+    boff[i] = (uint32_t)gr * (uint32_t)K + 16u * (uint32_t)((lane & 3) + 4 * (q & 1));
+  }
+  const int srow = (wave * 64) % BM;                 // a_s rows this wave stages
+  const int sr = (m0 + srow + lane) < M ? (m0 + srow + lane) : (M - 1);
+  const uint32_t soff = (uint32_t)sr * (uint32_t)G * 4u;
+  // b_s of the tile's column blocks, staged the same way (lane l holds
+  // block n0/128 + l, clamped), so the loop issues no scalar-memory loads.
+  const int bblk = ((n0 >> 7) + lane) < nblk ? ((n0 >> 7) + lane) : (nblk - 1);
+  const uint32_t bsoff = (uint32_t)bblk * (uint32_t)G * 4u;
 
-  v4i ra[A_PER_T], rb[B_PER_T];
-  float ras = 0.f;
-  auto gload = [&](int g) {
-    const int k0 = g * kGroup;
+  // LDS destinations are formed in the LDS address space from the array
+  // itself (the load writes lane l's bytes at dst + l * size).
+  lds_u8* const lds = (lds_u8*)smem;
+  const buf_rsrc rA = make_rsrc(Atile), rB = make_rsrc(Btile), rAs = make_rsrc(a_s), rBs = make_rsrc(b_s);
+  auto issue = [&](int g, int st) {
+    lds_u8* base = lds + st * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const v4i*>(pa[i] + k0);
+    for (int i = 0; i < A_PER_T; ++i) lds_dma16(rA, aoff[i], g * kGroup, base + 1024 * (i * NW + wave));
 #pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) rb[i] = *reinterpret_cast<const v4i*>(pb[i] + k0);
-    if (tid < BM) ras = pas[g];
-  };
-  auto lstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) *reinterpret_cast<v4i*>(sA[st] + 16 * (tid + i * NT)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) *reinterpret_cast<v4i*>(sB[st] + 16 * (tid + i * NT)) = rb[i];
-    if (tid < BM) sAs[st][tid] = ras;
+    for (int i = 0; i < B_PER_T; ++i) lds_dma16(rB, boff[i], g * kGroup, base + A_BYTES + 1024 * (i * NW + wave));
+    lds_dma4(rAs, soff, 4 * g, base + A_BYTES + B_BYTES + 4 * srow);
+    lds_dma4(rBs, bsoff, 4 * g, base + A_BYTES + B_BYTES + 4 * BM);
   };
 
   v4f acc[IB][JB];
@@ -82,39 +113,83 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_generic(
   for (int i = 0; i < IB; ++i)
 #pragma unroll
     for (int j = 0; j < JB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // fold(P, s, a): a = fma(P, s, a) elementwise, the group's contribution.
+  auto fold = [](v4f& a, const v4f& P, const float* s) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = __builtin_fmaf(P[r], s[r], a[r]);
+  };
+  // The partial of the last block of a group is folded after the first MFMA
+  // of the next group (zero partial and zero scale before the first group).
+  v4f pc = v4f{0.f, 0.f, 0.f, 0.f};
+  float scc[4] = {0.f, 0.f, 0.f, 0.f};
 
-  if (G > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < G) issue(p, p);
+
   for (int g = 0; g < G; ++g) {
-    const int cur = g & 1;
-    if (g + 1 < G) gload(g + 1);
-    const float bsv = b_s[(int64_t)nb * G + g];
-    float s[IB][4];
-#pragma unroll
-    for (int i = 0; i < IB; ++i) {
-      const v4f a4 = *reinterpret_cast<const v4f*>(&sAs[cur][wm * WM + 16 * i + 4 * (lane >> 4)]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[i][r] = a4[r] * bsv;
-    }
+    const int st = g % STAGES;
+    // This wave's loads of group g are done once at most the loads of the
+    // groups issued after it (up to STAGES-2 of them) are outstanding.
+    const int later = (G - 1 - g) < (STAGES - 2) ? (G - 1 - g) : (STAGES - 2);
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * LPG));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(LPG));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    // A bare barrier: the LDS writes that matter (group g's) are already
+    // complete; a fenced __syncthreads would also wait for group g+1's loads.
+    __builtin_amdgcn_s_barrier();
+    if (g + STAGES - 1 < G) issue(g + STAGES - 1, (g + STAGES - 1) % STAGES);
+
+    const uint8_t* base = smem + st * STAGE_BYTES;
+    const float* sAs = reinterpret_cast<const float*>(base + A_BYTES + B_BYTES);
+    const float bsv = sAs[BM + (nb - (n0 >> 7))];
+    // All B fragments of the wave's columns, then the row blocks in order,
+    // each one's A fragment and a_s row read a block ahead of its MFMAs.
     v8i bf[JB];
 #pragma unroll
-    for (int j = 0; j < JB; ++j) bf[j] = load_frag_lds(sB[cur], wn * WN + 16 * j, lane);
+    for (int j = 0; j < JB; ++j) bf[j] = load_frag_lds_fm(base + A_BYTES, (wn * WN) / 16 + j, lane);
+    v8i af = load_frag_lds_fm(base, (wm * WM) / 16, lane);
+    v4f a4 = *reinterpret_cast<const v4f*>(&sAs[wm * WM + 4 * (lane >> 4)]);
+    // Each MFMA's partial is folded after the next MFMA is issued, so the
+    // fold never waits on the MFMA that produces its operand.
+    v4f pp = pc;
+    float scp[4], sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) scp[r] = scc[r];
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
-      const v8i af = load_frag_lds(sA[cur], wm * WM + 16 * i, lane);
+      v8i af_next;
+      v4f a4_next;
+      if (i + 1 < IB) {
+        af_next = load_frag_lds_fm(base, (wm * WM) / 16 + i + 1, lane);
+        a4_next = *reinterpret_cast<const v4f*>(&sAs[wm * WM + 16 * (i + 1) + 4 * (lane >> 4)]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = a4[r] * bsv;
 #pragma unroll
       for (int j = 0; j < JB; ++j) {
+        // MFMA, then the previous partial's fold, in this order: left alone,
+        // the scheduler pulls each MFMA's own fold up next to it (to free
+        // registers early) and every fold stalls on its MFMA.
         const v4f p = mfma_group(af, bf[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j == 0) fold(i == 0 ? acc[IB - 1][JB - 1] : acc[i - 1][JB - 1], pp, scp);
+        else fold(acc[i][j - 1], pp, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        pp = p;
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], s[i][r], acc[i][j][r]);
+      for (int r = 0; r < 4; ++r) scp[r] = sc[r];
+      if (i + 1 < IB) {
+        af = af_next;
+        a4 = a4_next;
       }
     }
-    if (g + 1 < G) lstore(cur ^ 1);
-    __syncthreads();
+    pc = pp;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) scc[r] = sc[r];
   }
+  fold(acc[IB - 1][JB - 1], pc, scc);
 
   // P[i][j] = sum A[m_i] B[n_j]: lane holds m = 4*(lane>>4)+r, n = lane & 15 of each block.
 #pragma unroll
@@ -387,20 +462,20 @@ __global__ void k_fill_zero(void* __restrict__ C, int64_t count) {
 // ===========================================================================
 // Launchers
 // ===========================================================================
-template <int BM, int BN, int WM_, int WN_>
+template <int BM, int BN, int WM_, int WN_, int ST>
 static hipError_t launch_generic_t(const GemmArgs& a, int64_t grid, int band) {
   const dim3 blk(64 * WM_ * WN_);
   switch (a.out) {
     case kOutBF16:
-      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, kOutBF16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutBF16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
                          a.b_s, a.C, a.M, a.N, a.K, band);
       break;
     case kOutFP16:
-      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, kOutFP16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutFP16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
                          a.b_s, a.C, a.M, a.N, a.K, band);
       break;
     default:
-      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, kOutFP32>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutFP32>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
                          a.b_s, a.C, a.M, a.N, a.K, band);
   }
   return hipGetLastError();
@@ -408,8 +483,8 @@ static hipError_t launch_generic_t(const GemmArgs& a, int64_t grid, int band) {
 
 hipError_t launch_generic(const GemmArgs& a, int cfg, int64_t grid, int band) {
   switch (cfg) {
-#define X(id, bm, bn, wm, wn) \
-  case id: return launch_generic_t<bm, bn, wm, wn>(a, grid, band);
+#define X(id, bm, bn, wm, wn, st) \
+  case id: return launch_generic_t<bm, bn, wm, wn, st>(a, grid, band);
     FBG_GENERIC_CFGS(X)
 #undef X
     default: return hipErrorInvalidValue;

@@ -39,10 +39,13 @@ int swap_cfg_for(int64_t M) { return M <= 64 ? 2 : 4; }
 // above, 16 n x 64 m with 2 waves taking one group each (config 5).
 int short_cfg_for(int64_t M) { return M <= 48 ? 2 : 5; }
 
+// Generic: the largest tile that still gives every compute unit a
+// workgroup -- 256 x 256 (8 waves, the highest MFMA work per LDS byte),
+// then 256 x 128, then 128 x 128; 64 x 128 for M <= 64.
 int generic_cfg_for(int64_t M, int64_t N, int cu) {
   if (M <= 64) return 2;
-  const int64_t t256x128 = cdiv(M, 256) * cdiv(N, 128);
-  if (t256x128 >= 2 * (int64_t)cu) return 1;
+  if (cdiv(M, 256) * cdiv(N, 256) >= (int64_t)cu) return 3;
+  if (cdiv(M, 256) * cdiv(N, 128) >= (int64_t)cu) return 1;
   return 0;
 }
 

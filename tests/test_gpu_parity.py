@@ -29,6 +29,8 @@ TOL_CASES = [
     ("generic", 1, 300, 260, 256, 0),
     ("generic", 2, 17, 1000, 256, 0),
     ("generic", 2, 1, 130, 128, 0),
+    ("generic", 3, 300, 520, 640, 0),
+    ("generic", 3, 513, 257, 256, 0),
     ("short_k256", 0, 184, 700, 256, 0),
     ("short_k256", 0, 300, 515, 256, 0),
     ("short_k256", 1, 37, 130, 256, 0),
@@ -95,6 +97,7 @@ def test_variant_within_tolerance(gpu, case, out):
 EXACT_CASES = [
     ("generic", 0, 150, 300, 1024, 0),
     ("generic", 2, 40, 260, 512, 0),
+    ("generic", 3, 260, 300, 768, 0),
     ("short_k256", 0, 100, 640, 256, 0),
     ("short_k256", 2, 5, 130, 256, 0),
     ("short_k256", 7, 128, 256, 256, 0),
