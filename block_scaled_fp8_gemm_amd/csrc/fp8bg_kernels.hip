@@ -25,20 +25,28 @@ namespace fbg {
 //
 // Loads go straight from global memory into LDS (buffer_load_dwordx4 ... lds):
 // no staging registers and no LDS store instructions.  Every thread issues
-// the same LPG loads per group (A slots, B slots and one a_s load), so one
-// vmcnt bound per step says "this wave's loads of group g have landed"; a
-// barrier then makes the whole tile visible.  The loads of group g+STAGES-1
-// are issued once group g's tile is in LDS, into the slot every wave
-// finished reading in the previous step.
+// the same LPG loads per group (A images, B images, one a_s and one b_s
+// load), so one vmcnt bound says "this wave's loads of group g have landed";
+// a barrier then makes the whole tile visible.  The one barrier per group
+// sits in the group's last row block, once every LDS read of the group has
+// been issued: past it, the slot is refilled with the group STAGES ahead,
+// and the next group's scales and fragments are read while the last
+// block's MFMAs run, so a group starts with its operands in registers.
+//
+// Operand order: weight rows n on the MFMA's first operand, activation rows
+// m on the second, so a lane ends with ONE output row m and 4 consecutive
+// columns n of each 16x16 block.  The block's scale a_s[m,g] * b_s[n/128,g]
+// is then one value per lane (a wave's columns share one b_s block), the
+// a_s of a lane's rows is one short LDS read per group, and the epilogue
+// stores 4 outputs per lane at once.
 //
 // Each MFMA writes a fresh FP32 partial; its fold acc = fma(P, s, acc) is
-// issued one block behind, in the shadow of the next MFMA (the schedule is
-// pinned with sched_group_barrier), so the VALU fold overlaps the MFMA pipe.
+// issued after the next MFMA, in that MFMA's shadow.
 // ===========================================================================
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int OUT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
     const uint8_t* __restrict__ A, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
-    const float* __restrict__ b_s, void* __restrict__ C, int M, int N, int K, int band) {
+    const float* __restrict__ b_s, void* __restrict__ C, int M, int N, int K, int band, int vec_ok) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -47,11 +55,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   constexpr int LPG = A_PER_T + B_PER_T + 2;         // vector-memory loads per group per thread
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, S_BYTES = BM * 4 + 64 * 4;
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile slots must split evenly over threads");
+  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile images must split evenly over waves");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one b_s block");
   static_assert(BM >= 64 && BM % 64 == 0, "a_s rows are staged 64 per wave instruction");
+  static_assert(IB == 4 || IB == 8, "a lane reads its row scales as one or two 16-byte words");
   static_assert(STAGES >= 2 && STAGES <= 4 && STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring must fit in 160 KB");
-  static_assert(2 * LPG < 64, "vmcnt counts at most 63 outstanding loads");
+  static_assert((STAGES - 1) * LPG < 64, "vmcnt counts at most 63 outstanding loads");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[STAGES * STAGE_BYTES];
 
@@ -86,11 +95,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
     const int gr = (n0 + r) < N ? r : (N - 1 - n0);
     boff[i] = (uint32_t)gr * (uint32_t)K + 16u * (uint32_t)((lane & 3) + 4 * (q & 1));
   }
-  const int srow = (wave * 64) % BM;                 // a_s rows this wave stages
-  const int sr = (m0 + srow + lane) < M ? (m0 + srow + lane) : (M - 1);
+  // a_s of the tile's rows, staged transposed: slot (w*16 + r)*IB + i holds
+  // row w*WM + 16*i + r, so the IB row scales a lane needs (its row r = l & 15
+  // in each of its wave's row blocks) are contiguous.  Wave w stages slots
+  // (64w mod BM) + lane.
+  const int slot = (wave * 64) % BM + lane;
+  const int srow = (slot / (16 * IB)) * WM + 16 * (slot % IB) + (slot / IB) % 16;
+  const int sr = (m0 + srow) < M ? (m0 + srow) : (M - 1);
   const uint32_t soff = (uint32_t)sr * (uint32_t)G * 4u;
-  // b_s of the tile's column blocks, staged the same way (lane l holds
-  // block n0/128 + l, clamped), so the loop issues no scalar-memory loads.
+  // b_s of the tile's column blocks (lane l holds block n0/128 + l, clamped),
+  // so the loop issues no scalar-memory loads.
   const int bblk = ((n0 >> 7) + lane) < nblk ? ((n0 >> 7) + lane) : (nblk - 1);
   const uint32_t bsoff = (uint32_t)bblk * (uint32_t)G * 4u;
 
@@ -104,7 +118,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
     for (int i = 0; i < A_PER_T; ++i) lds_dma16(rA, aoff[i], g * kGroup, base + 1024 * (i * NW + wave));
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) lds_dma16(rB, boff[i], g * kGroup, base + A_BYTES + 1024 * (i * NW + wave));
-    lds_dma4(rAs, soff, 4 * g, base + A_BYTES + B_BYTES + 4 * srow);
+    lds_dma4(rAs, soff, 4 * g, base + A_BYTES + B_BYTES + 4 * ((wave * 64) % BM));
     lds_dma4(rBs, bsoff, 4 * g, base + A_BYTES + B_BYTES + 4 * BM);
   };
 
@@ -113,95 +127,117 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   for (int i = 0; i < IB; ++i)
 #pragma unroll
     for (int j = 0; j < JB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  // fold(P, s, a): a = fma(P, s, a) elementwise, the group's contribution.
-  auto fold = [](v4f& a, const v4f& P, const float* s) {
+  // fold(a, P, s): a = fma(P, s, a) elementwise, the group's contribution.
+  auto fold = [](v4f& a, const v4f& P, float s) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = __builtin_fmaf(P[r], s[r], a[r]);
+    for (int r = 0; r < 4; ++r) a[r] = __builtin_fmaf(P[r], s, a[r]);
   };
-  // The partial of the last block of a group is folded after the first MFMA
-  // of the next group (zero partial and zero scale before the first group).
-  v4f pc = v4f{0.f, 0.f, 0.f, 0.f};
-  float scc[4] = {0.f, 0.f, 0.f, 0.f};
+  // The partial of a group's last block is folded after the first MFMA of
+  // the next group (zero partial and zero scale before the first group).
+  v4f pp = v4f{0.f, 0.f, 0.f, 0.f};
+  float scp = 0.f;
 
+  // Head of a group: what its first MFMAs need, read from its LDS slot --
+  // the lane's row scales, the b_s of the wave's columns, the first A
+  // fragment (the B fragments are read one by one by the caller).
+  float as[IB], bsv;
+  v8i bf[JB], af;
+  auto read_head = [&](int st, float* as_o, float& bsv_o, v8i& af_o) {
+    const uint8_t* base = smem + st * STAGE_BYTES;
+    const float* sS = reinterpret_cast<const float*>(base + A_BYTES + B_BYTES);
+    bsv_o = sS[BM + (nb - (n0 >> 7))];
+    const v4f* ps = reinterpret_cast<const v4f*>(sS + (wm * 16 + (lane & 15)) * IB);
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < G) issue(p, p);
+    for (int q = 0; q < IB / 4; ++q) {
+      const v4f v = ps[q];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) as_o[4 * q + r] = v[r];
+    }
+    af_o = load_frag_lds_fm(base, (wm * WM) / 16, lane);
+  };
+  auto read_b = [&](int st, int j) {
+    return load_frag_lds_fm(smem + st * STAGE_BYTES + A_BYTES, (wn * WN) / 16 + j, lane);
+  };
+
+  // Slot s holds group s, s + STAGES, ...  Every slot is filled up front;
+  // group g's slot is refilled with group g + STAGES at g's switch point.
+  // Refills past the last group load the last group again into a slot no
+  // wave reads any more: the loop body stays a single basic block (a branch
+  // there lets the compiler sink every fold below it), and the number of
+  // loads in flight is the same at every switch point.
+  auto grp = [&](int g) { return g < G ? g : G - 1; };
+#pragma unroll
+  for (int p = 0; p < STAGES; ++p) issue(grp(p), p);
+  // Group 0 has landed once at most the later slots' loads are outstanding.
+  __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 1) * LPG));
+  __builtin_amdgcn_s_barrier();
+  read_head(0, as, bsv, af);
+#pragma unroll
+  for (int j = 0; j < JB; ++j) bf[j] = read_b(0, j);
 
   for (int g = 0; g < G; ++g) {
-    const int st = g % STAGES;
-    // This wave's loads of group g are done once at most the loads of the
-    // groups issued after it (up to STAGES-2 of them) are outstanding.
-    const int later = (G - 1 - g) < (STAGES - 2) ? (G - 1 - g) : (STAGES - 2);
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * LPG));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(LPG));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-    // A bare barrier: the LDS writes that matter (group g's) are already
-    // complete; a fenced __syncthreads would also wait for group g+1's loads.
-    __builtin_amdgcn_s_barrier();
-    if (g + STAGES - 1 < G) issue(g + STAGES - 1, (g + STAGES - 1) % STAGES);
-
+    const int st = g % STAGES, nst = (g + 1) % STAGES;
     const uint8_t* base = smem + st * STAGE_BYTES;
-    const float* sAs = reinterpret_cast<const float*>(base + A_BYTES + B_BYTES);
-    const float bsv = sAs[BM + (nb - (n0 >> 7))];
-    // All B fragments of the wave's columns, then the row blocks in order,
-    // each one's A fragment and a_s row read a block ahead of its MFMAs.
-    v8i bf[JB];
-#pragma unroll
-    for (int j = 0; j < JB; ++j) bf[j] = load_frag_lds_fm(base + A_BYTES, (wn * WN) / 16 + j, lane);
-    v8i af = load_frag_lds_fm(base, (wm * WM) / 16, lane);
-    v4f a4 = *reinterpret_cast<const v4f*>(&sAs[wm * WM + 4 * (lane >> 4)]);
-    // Each MFMA's partial is folded after the next MFMA is issued, so the
-    // fold never waits on the MFMA that produces its operand.
-    v4f pp = pc;
-    float scp[4], sc[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) scp[r] = scc[r];
+    float as_n[IB], bsv_n;
+    v8i af_n;
+    float sc = 0.f;
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
       v8i af_next;
-      v4f a4_next;
-      if (i + 1 < IB) {
-        af_next = load_frag_lds_fm(base, (wm * WM) / 16 + i + 1, lane);
-        a4_next = *reinterpret_cast<const v4f*>(&sAs[wm * WM + 16 * (i + 1) + 4 * (lane >> 4)]);
+      if (i + 1 < IB) af_next = load_frag_lds_fm(base, (wm * WM) / 16 + i + 1, lane);
+      sc = as[i] * bsv;
+      if (i == IB - 1) {
+        // Switch point: every LDS read of this group's slot has been issued.
+        // Wait for them and for group g+1's loads (the later groups' loads
+        // may stay outstanding), so that past the barrier g+1's tile is
+        // visible and no wave reads slot st any more: refill it with group
+        // g + STAGES, and read g+1's head while this block's MFMAs run.
+        // (After the last group the head reads fetch a stale slot; the
+        // values are never used.)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 2) * LPG) & ~(15 << 8));
+        __builtin_amdgcn_s_barrier();
+        issue(grp(g + STAGES), st);
+        read_head(nst, as_n, bsv_n, af_n);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = a4[r] * bsv;
 #pragma unroll
       for (int j = 0; j < JB; ++j) {
         // MFMA, then the previous partial's fold, in this order: left alone,
         // the scheduler pulls each MFMA's own fold up next to it (to free
         // registers early) and every fold stalls on its MFMA.
-        const v4f p = mfma_group(af, bf[j]);
+        const v4f p = mfma_group(bf[j], af);
         __builtin_amdgcn_sched_barrier(0);
         if (j == 0) fold(i == 0 ? acc[IB - 1][JB - 1] : acc[i - 1][JB - 1], pp, scp);
         else fold(acc[i][j - 1], pp, sc);
+        // In the last block, B fragment j of the next group replaces this
+        // one once its MFMA has been issued.
+        if (i == IB - 1) bf[j] = read_b(nst, j);
         __builtin_amdgcn_sched_barrier(0);
         pp = p;
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) scp[r] = sc[r];
-      if (i + 1 < IB) {
-        af = af_next;
-        a4 = a4_next;
-      }
+      scp = sc;
+      if (i + 1 < IB) af = af_next;
     }
-    pc = pp;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) scc[r] = sc[r];
+    for (int i = 0; i < IB; ++i) as[i] = as_n[i];
+    bsv = bsv_n;
+    af = af_n;
   }
-  fold(acc[IB - 1][JB - 1], pc, scc);
+  fold(acc[IB - 1][JB - 1], pp, scp);
+  // The refills issued past the last group must land before the workgroup
+  // ends and its LDS is handed to another.
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
 
-  // P[i][j] = sum A[m_i] B[n_j]: lane holds m = 4*(lane>>4)+r, n = lane & 15 of each block.
+  // Block (i, j): lane holds row m = 16*i + (lane & 15), columns
+  // n = 16*j + 4*(lane >> 4) + r, r = 0..3, of the wave's sub-tile.
+  const int m_l = m0 + wm * WM + (lane & 15);
+  const int n_l = n0 + wn * WN + 4 * (lane >> 4);
 #pragma unroll
   for (int i = 0; i < IB; ++i)
 #pragma unroll
     for (int j = 0; j < JB; ++j) {
-      const int n = n0 + wn * WN + 16 * j + (lane & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * WM + 16 * i + 4 * (lane >> 4) + r;
-        if (m < M && n < N) store1<OUT>(C, (int64_t)m * N + n, acc[i][j][r]);
-      }
+      const int m = m_l + 16 * i, n = n_l + 16 * j;
+      const int cnt = (N - n) < 4 ? (N - n) : 4;
+      if (m < M && cnt > 0) store4<OUT>(C, (int64_t)m * N + n, acc[i][j], cnt, vec_ok);
     }
 }
 
@@ -468,15 +504,15 @@ static hipError_t launch_generic_t(const GemmArgs& a, int64_t grid, int band) {
   switch (a.out) {
     case kOutBF16:
       hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutBF16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
-                         a.b_s, a.C, a.M, a.N, a.K, band);
+                         a.b_s, a.C, a.M, a.N, a.K, band, a.vec);
       break;
     case kOutFP16:
       hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutFP16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
-                         a.b_s, a.C, a.M, a.N, a.K, band);
+                         a.b_s, a.C, a.M, a.N, a.K, band, a.vec);
       break;
     default:
       hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutFP32>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
-                         a.b_s, a.C, a.M, a.N, a.K, band);
+                         a.b_s, a.C, a.M, a.N, a.K, band, a.vec);
   }
   return hipGetLastError();
 }
