@@ -55,7 +55,11 @@ namespace fbg {
   X(8, 2, 12, 2, 1)       \
   X(9, 1, 12, 2, 1)       \
   X(10, 2, 4, 2, 1)       \
-  X(11, 4, 4, 2, 1)
+  X(11, 4, 4, 2, 1)       \
+  X(12, 1, 1, 2, 1)       \
+  X(13, 2, 1, 2, 1)       \
+  X(14, 1, 2, 2, 1)       \
+  X(15, 2, 2, 2, 1)
 
 struct GenericCfg { int bm, bn, waves_m, waves_n, stages; };
 constexpr GenericCfg kGenericCfgs[] = {

@@ -258,8 +258,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 // chunks kw, kw+KW, ...); their FP32 partials are summed through LDS in the
 // fixed order kw = 0..KW-1.
 //
-// Split-K over workgroups (S > 1): workgroup (tile, s) covers groups
-// [s*G/S, (s+1)*G/S) and publishes its FP32 partial at device scope; the last
+// Split-K over workgroups (S > 1): workgroup (tile, s) covers a contiguous
+// run of G/S or G/S + 1 groups (the first G%S splits take one more) and
+// publishes its FP32 partial at device scope; the last
 // of the S workgroups of a tile to arrive (one counter atomic per workgroup,
 // no atomics on data) sums the S partials in the fixed order s = 0..S-1,
 // casts, stores and resets the counter.  The page's split-K summed partials
@@ -292,9 +293,15 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
   const int T = tiles_n * tiles_m;
   const int lid = xcd_remap(blockIdx.x, T * S);
   const int s = lid / T, tile = lid - s * T;
-  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+  // The m-tiles of one n-tile are consecutive, so they run on one XCD and
+  // the weight rows they share are fetched from HBM once, then hit its L2.
+  const int tn = tile / tiles_m, tm = tile - tn * tiles_m;
   const int m0 = tm * BMS, n0 = tn * BN;
-  const int g_lo = (int)((int64_t)s * G / S), g_hi = (int)((int64_t)(s + 1) * G / S);
+  // Split s takes G/S groups, one more for the first G%S splits (32-bit
+  // arithmetic: a 64-bit division here costs hundreds of scalar cycles at
+  // every workgroup's start).
+  const int gq = G / S, gr = G - gq * S;
+  const int g_lo = s * gq + (s < gr ? s : gr), g_hi = g_lo + gq + (s < gr ? 1 : 0);
   const int nblk = (N + 127) / 128;
   const int nb = (n0 >> 7) < nblk ? (n0 >> 7) : nblk - 1;
   const int64_t ldk = KFIX ? (int64_t)KFIX * kGroup : (int64_t)K;
@@ -447,25 +454,33 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
     }
     __syncthreads();
     if (!sLast) return;
-    // Last arrival: sum the S partials in the fixed order q = 0..S-1, all
-    // loads of one split issued before its adds.
+    // Last arrival: sum the S partials in the fixed order q = 0..S-1.  The
+    // partials are loaded QB splits at a time, every load of a batch issued
+    // before its adds (split indices past S-1 reload split S-1 and are not
+    // added), so S <= QB costs one memory round trip.
+    constexpr int QB = 4;
     const float* wt = ws + (int64_t)tile * TILE_ELEMS;
     const int64_t split_stride = (int64_t)T * TILE_ELEMS;
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
       if (b % KW != kw) continue;
-      v4f v;
+      v4f v = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int q0 = 0; q0 < S; q0 += QB) {
+        v4f t[QB];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        v[r] = __hip_atomic_load(wt + (b * 4 + r) * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int q = 1; q < S; ++q) {
-        v4f t;
+        for (int u = 0; u < QB; ++u) {
+          const int q = (q0 + u) < S ? (q0 + u) : (S - 1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          t[r] = __hip_atomic_load(wt + q * split_stride + (b * 4 + r) * 64 + lane, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+          for (int r = 0; r < 4; ++r)
+            t[u][r] = __hip_atomic_load(wt + q * split_stride + (b * 4 + r) * 64 + lane, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] += t[r];
+        for (int u = 0; u < QB; ++u) {
+          if (q0 + u >= S) break;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = (q0 + u == 0) ? t[u][r] : v[r] + t[u][r];
+        }
       }
       acc[b / MB16][b % MB16] = v;
     }

@@ -26,27 +26,42 @@ int64_t skinny_tiles(const SkinnyCfg& c, int64_t M, int64_t N) {
   return cdiv(N, skinny_tile_n(c)) * cdiv(M, skinny_tile_m(c));
 }
 
-// Tile configurations of the skinny family, from the configuration sweeps
-// of the decode, short-K and mid-M shapes (bench.py with forced variant,
-// split and configuration; every point kept in profiles/):
-//  - M <= 64: 16 n x 16 m tiles with 4 waves splitting K (swap-AB config 2);
-//    narrow tiles give the most workgroups, which beats streaming each
-//    weight row only once;
-//  - M <= 128: 32 n x 64 m tiles, 2 waves (config 4).
-int swap_cfg_for(int64_t M) { return M <= 64 ? 2 : 4; }
+// Tile configurations, from on-device configuration sweeps of every
+// workload shape and sweep point (bench.py with forced variant, split and
+// configuration; the results are kept in profiles/).  The small shapes are
+// bound by how many bytes each compute unit must pull (each CU sustains
+// ~25-28 GB/s at these sizes) plus the split-K handshake, so the rules
+// pick the tile that fills the device with the fewest bytes per CU.
+//
+// Swap-AB: 32 n x 64 m tiles (config 4) read every weight row once for
+// M <= 64 and are used when they alone give every CU a workgroup (M > 16);
+// otherwise 32 n x 16 m tiles (config 7), split over K below until the
+// grid covers the device.
+int swap_cfg_for(int64_t M, int64_t N, int cu) {
+  if (M > 16 && cdiv(N, 32) * cdiv(M, 64) >= (int64_t)cu) return 4;
+  return 7;
+}
 
-// Short-K: 16 n x 16 m, one wave, both groups (config 2) up to M = 48;
-// above, 16 n x 64 m with 2 waves taking one group each (config 5).
-int short_cfg_for(int64_t M) { return M <= 48 ? 2 : 5; }
+// Short-K (two groups, one per wave): 16 n x 16 m up to M = 48 (config 12),
+// 32 n x 32 m up to M = 200 (config 15), 32 n x 64 m up to M = 256
+// (config 10); above, 32 n x 32 m with one wave taking both groups
+// (config 6).
+int short_cfg_for(int64_t M) {
+  if (M <= 48) return 12;
+  if (M <= 200) return 15;
+  if (M <= 256) return 10;
+  return 6;
+}
 
 // Generic: the largest tile that still gives every compute unit a
 // workgroup -- 256 x 256 (8 waves, the highest MFMA work per LDS byte),
-// then 256 x 128, then 128 x 128; 64 x 128 for M <= 64.
+// then 256 x 128, then 128 x 128 -- else 64 x 128 (the most workgroups).
 int generic_cfg_for(int64_t M, int64_t N, int cu) {
   if (M <= 64) return 2;
   if (cdiv(M, 256) * cdiv(N, 256) >= (int64_t)cu) return 3;
   if (cdiv(M, 256) * cdiv(N, 128) >= (int64_t)cu) return 1;
-  return 0;
+  if (cdiv(M, 128) * cdiv(N, 128) >= (int64_t)cu) return 0;
+  return 2;
 }
 
 }  // namespace
@@ -79,10 +94,12 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
 
   int v = variant;
   if (v == FBG_VARIANT_AUTO) {
+    // Swap-AB (maybe split over K below) for M <= 64, and up to M = 128 when
+    // the generic kernel's smallest tile would leave over half the device idle.
     if (K == 256 && M <= 1024)
       v = FBG_VARIANT_SHORT_K256;
-    else if (M <= 128)
-      v = FBG_VARIANT_SWAP_AB;  // may become split-K below
+    else if (M <= 64 || (M <= 128 && cdiv(M, 64) * cdiv(N, 128) < (int64_t)cu / 2))
+      v = FBG_VARIANT_SWAP_AB;
     else
       v = FBG_VARIANT_GENERIC;
   }
@@ -110,7 +127,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
     out->waves = k.kw;
     out->grid = skinny_tiles(k, M, N);
   } else {  // SWAP_AB or SWAP_AB_SPLITK
-    const int c = force_cfg >= 0 ? force_cfg : swap_cfg_for(M);
+    const int c = force_cfg >= 0 ? force_cfg : swap_cfg_for(M, N, cu);
     const SkinnyCfg& k = kSwapCfgs[c];
     const int64_t tiles = skinny_tiles(k, M, N);
     int64_t S = 1;
