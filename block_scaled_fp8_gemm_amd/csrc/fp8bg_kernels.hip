@@ -7,7 +7,7 @@
 // idea".)  The pages' kernels were Hopper/Triton designs; these are written
 // for CDNA4: 64-lane waves, the 16x16x128 FP8 MFMA (one MFMA consumes exactly
 // one 128-wide scale group, so its output is the group's fresh partial),
-// fragment-major LDS tiles, and XCD-aware workgroup placement.
+// swizzled LDS tiles, and XCD-aware workgroup placement.
 //
 // Every kernel computes, per output element, the same FP32 chain
 //   acc = 0; for g in its group range: acc = fma(P_g, a_s[m,g] * b_s[n/128,g], acc)
@@ -77,23 +77,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 
   // Per-lane 32-bit source offsets inside the tile's rows (rows past the
   // matrix are clamped to its last row: they feed outputs never stored).
-  // Load q (q = i*NW + wave) fills fragment-major image q: row block q >> 1,
-  // half q & 1; lane l supplies row 16*(q>>1) + (l >> 2), bytes
-  // 64*(q & 1) + 16*(l & 3).
+  // Load q (q = i*NW + wave) fills LDS bytes [1024q, 1024q + 1024) of the
+  // tile: rows 8q .. 8q+7; lane l writes row 8q + (l >> 3), slot l & 7, so it
+  // reads the row's chunk (l & 7) ^ s(row).
   const uint8_t* Atile = A + (int64_t)m0 * K;
   const uint8_t* Btile = B + (int64_t)n0 * K;
   uint32_t aoff[A_PER_T], boff[B_PER_T];
 #pragma unroll
   for (int i = 0; i < A_PER_T; ++i) {
-    const int q = i * NW + wave, r = 16 * (q >> 1) + (lane >> 2);
+    const int r = 8 * (i * NW + wave) + (lane >> 3);
     const int gr = (m0 + r) < M ? r : (M - 1 - m0);
-    aoff[i] = (uint32_t)gr * (uint32_t)K + 16u * (uint32_t)((lane & 3) + 4 * (q & 1));
+    aoff[i] = (uint32_t)gr * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ swz_row(r));
   }
 #pragma unroll
   for (int i = 0; i < B_PER_T; ++i) {
-    const int q = i * NW + wave, r = 16 * (q >> 1) + (lane >> 2);
+    const int r = 8 * (i * NW + wave) + (lane >> 3);
     const int gr = (n0 + r) < N ? r : (N - 1 - n0);
-    boff[i] = (uint32_t)gr * (uint32_t)K + 16u * (uint32_t)((lane & 3) + 4 * (q & 1));
+    boff[i] = (uint32_t)gr * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ swz_row(r));
   }
   // a_s of the tile's rows, staged transposed: slot (w*16 + r)*IB + i holds
   // row w*WM + 16*i + r, so the IB row scales a lane needs (its row r = l & 15
@@ -153,10 +153,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 #pragma unroll
       for (int r = 0; r < 4; ++r) as_o[4 * q + r] = v[r];
     }
-    af_o = load_frag_lds_fm(base, (wm * WM) / 16, lane);
+    af_o = load_frag_lds_sw(base, wm * WM, lane);
   };
   auto read_b = [&](int st, int j) {
-    return load_frag_lds_fm(smem + st * STAGE_BYTES + A_BYTES, (wn * WN) / 16 + j, lane);
+    return load_frag_lds_sw(smem + st * STAGE_BYTES + A_BYTES, wn * WN + 16 * j, lane);
   };
 
   // Slot s holds group s, s + STAGES, ...  Every slot is filled up front;
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
       v8i af_next;
-      if (i + 1 < IB) af_next = load_frag_lds_fm(base, (wm * WM) / 16 + i + 1, lane);
+      if (i + 1 < IB) af_next = load_frag_lds_sw(base, wm * WM + 16 * (i + 1), lane);
       sc = as[i] * bsv;
       if (i == IB - 1) {
         // Switch point: every LDS read of this group's slot has been issued.
