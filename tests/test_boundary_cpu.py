@@ -146,3 +146,22 @@ def test_python_wrapper_checks():
     with pytest.raises(ValueError):
         fbg.gemm(A, torch.zeros((4, 2)), torch.zeros((8, 256), dtype=torch.float8_e4m3fn)[:, ::1].t(),
                  torch.zeros((1, 2)))
+
+
+def test_every_tile_configuration_has_parity_cases():
+    """Every configuration the kernels can be launched with (the X-macro lists
+    of csrc/fp8bg_configs.h) is forced by at least one GPU tolerance case."""
+    text = open(os.path.join(ROOT, "block_scaled_fp8_gemm_amd", "csrc", "fp8bg_configs.h")).read()
+
+    def ids(macro):
+        body = re.search(r"#define %s\(X\)(.*?)\n\n" % macro, text, re.S).group(1)
+        return {int(i) for i in re.findall(r"X\((\d+),", body)}
+
+    from tests.test_gpu_parity import TOL_CASES
+    have = {}
+    for variant, cfg, *_ in TOL_CASES:
+        family = "swap_ab" if variant.startswith("swap_ab") else variant
+        have.setdefault(family, set()).add(cfg)
+    assert ids("FBG_GENERIC_CFGS") <= have["generic"]
+    assert ids("FBG_SWAP_CFGS") <= have["swap_ab"]
+    assert ids("FBG_SHORT_CFGS") <= have["short_k256"]

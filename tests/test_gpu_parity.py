@@ -70,6 +70,10 @@ TOL_CASES = [
     ("short_k256", 9, 184, 130, 256, 0),
     ("short_k256", 10, 70, 260, 256, 0),
     ("short_k256", 11, 64, 500, 256, 0),
+    ("short_k256", 12, 48, 515, 256, 0),
+    ("short_k256", 13, 33, 300, 256, 0),
+    ("short_k256", 14, 1, 700, 256, 0),
+    ("short_k256", 15, 184, 260, 256, 0),
     ("swap_ab_splitk", 0, 64, 512, 4096, 8),
     ("swap_ab_splitk", 0, 64, 512, 4096, 3),
     ("swap_ab_splitk", 1, 9, 1000, 2048, 16),
@@ -98,6 +102,7 @@ EXACT_CASES = [
     ("generic", 0, 150, 300, 1024, 0),
     ("generic", 2, 40, 260, 512, 0),
     ("generic", 3, 260, 300, 768, 0),
+    ("short_k256", 15, 100, 300, 256, 0),
     ("short_k256", 0, 100, 640, 256, 0),
     ("short_k256", 2, 5, 130, 256, 0),
     ("short_k256", 7, 128, 256, 256, 0),
