@@ -49,6 +49,11 @@ def _load():
     lib.fp8bg_oracle_round.restype = ctypes.c_int
     lib.fp8bg_oracle_round.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                        ctypes.c_void_p]
+    lib.fp8bg_oracle_e4m3_encode.restype = ctypes.c_uint
+    lib.fp8bg_oracle_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.fp8bg_oracle_quantize_rows.restype = None
+    lib.fp8bg_oracle_quantize_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_void_p, ctypes.c_void_p]
     lib.fp8bg_oracle_threads.restype = ctypes.c_int
     lib.fp8bg_oracle_threads.argtypes = []
     _lib = lib
@@ -142,3 +147,28 @@ def tolerance(C_ref, out_dtype) -> np.ndarray:
     C_ref = np.asarray(C_ref, dtype=np.float64)
     rms = float(np.sqrt(np.mean(np.square(C_ref)))) if C_ref.size else 0.0
     return 2.0 * ulp(C_ref, out_dtype) + 1e-3 * rms
+
+
+def e4m3_encode(x: float) -> int:
+    """OCP E4M3 code of a finite value, round to nearest even, saturating at
+    +-448 (fp8bg_oracle.c, fp8bg_oracle_e4m3_encode)."""
+    return int(_load().fp8bg_oracle_e4m3_encode(float(x)))
+
+
+def quantize_rows(x_bf16_bits):
+    """Per-token 1 x 128 activation quantisation (FlagGems-vllm PR #693,
+    section "Description": FP8 E4M3 activations with per-token scales).
+
+    x_bf16_bits: uint16 [M,K] bf16 bit patterns.  Returns (A, a_s): uint8
+    [M,K] E4M3 codes and float32 [M, ceil(K/128)] scales, with
+    a_s = max(amax, 1e-12)/448 per group and A = E4M3_RNE(clamp(x/a_s, +-448)),
+    both divisions in fp32.
+    """
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    M, K = x.shape
+    G = (K + GROUP - 1) // GROUP
+    q = np.empty((M, K), dtype=np.uint8)
+    a_s = np.empty((M, G), dtype=np.float32)
+    if M and K:
+        _load().fp8bg_oracle_quantize_rows(x.ctypes.data, M, K, q.ctypes.data, a_s.ctypes.data)
+    return q, a_s

@@ -29,6 +29,10 @@
  *
  * The cast to the output dtype is one IEEE round-to-nearest-even step from
  * the fp64 value (the pages only say "casts"; RNE is the reading taken).
+ *
+ * It also computes the producer of A and a_s, the per-token 1 x 128
+ * activation quantisation (fp8bg_oracle_quantize_rows, with the E4M3
+ * encoder fp8bg_oracle_e4m3_encode written from the format definition).
  */
 #include <math.h>
 #include <stdint.h>
@@ -172,6 +176,86 @@ int fp8bg_oracle_round(const double *x, int64_t n, int out_dtype, void *out)
 }
 
 /* Number of threads the OpenMP loop above uses. */
+/* ------------------------------------------------------------------------ */
+/* Per-token activation quantisation to E4M3 with one fp32 scale per row    */
+/* and 128-wide group: the producer of A and a_s (the pages' per-token      */
+/* 1 x 128 activation scales, FlagGems-vllm PR #693, section "Description").*/
+/*                                                                          */
+/*     amax   = max_{k in group} |x[m,k]|             (x: bf16 values)       */
+/*     a_s    = max(amax, 1e-12f) / 448               (fp32 division, RNE)   */
+/*     A[m,k] = E4M3_RNE(clamp(x[m,k] / a_s, -448, 448))   (fp32 division)  */
+/*                                                                          */
+/* 448 is E4M3's largest finite value, so the group's largest element maps  */
+/* to (about) +-448; the 1e-12 floor keeps an all-zero group finite; the    */
+/* clamp absorbs a quotient rounded just above 448.                         */
+/* ------------------------------------------------------------------------ */
+
+/* E4M3 code of a finite double with |x| <= 448, rounding to the nearest   */
+/* representable value, ties to the even code.  Written from the format:   */
+/* below 2^-6 the values are the multiples of 2^-9 (codes 0..8 carry on    */
+/* into the first binade); in the binade [2^e, 2^(e+1)) they are the       */
+/* multiples of 2^(e-3).                                                   */
+unsigned fp8bg_oracle_e4m3_encode(double x)
+{
+    const unsigned sign = signbit(x) ? 0x80u : 0u;
+    double a = fabs(x);
+    unsigned code;
+    if (a >= 448.0)
+        return sign | 0x7Eu;
+    if (a < ldexp(1.0, -6)) {
+        const double q = nearbyint(ldexp(a, 9));        /* units of 2^-9, 0..8 */
+        code = (unsigned)q;                              /* 8 is 2^-6 = e=1, m=0 */
+    } else {
+        int e2;
+        frexp(a, &e2);                                   /* a in [2^(e2-1), 2^e2) */
+        const int e = e2 - 1;                            /* unbiased exponent      */
+        double q = nearbyint(ldexp(a, 3 - e));           /* units of 2^(e-3): 8..16 */
+        int eb = e + 7;
+        if (q >= 16.0) {                                 /* rounded up to 2^(e+1) */
+            q = 8.0;
+            eb += 1;
+        }
+        code = ((unsigned)eb << 3) | ((unsigned)q - 8u);
+    }
+    return sign | code;
+}
+
+static float bf16_value(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* x: [M,K] bf16 bit patterns, row-major; q: [M,K] codes; a_s: [M, ceil(K/128)]. */
+void fp8bg_oracle_quantize_rows(const uint16_t *x, int64_t M, int64_t K,
+                                uint8_t *q, float *a_s)
+{
+    const int64_t G = (K + ORACLE_GROUP - 1) / ORACLE_GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t g = 0; g < G; ++g) {
+            const int64_t k0 = g * ORACLE_GROUP;
+            const int64_t k1 = k0 + ORACLE_GROUP < K ? k0 + ORACLE_GROUP : K;
+            float amax = 0.0f;
+            for (int64_t i = k0; i < k1; ++i) {
+                const float v = fabsf(bf16_value(x[m * K + i]));
+                if (v > amax)
+                    amax = v;
+            }
+            const float s = (amax > 1e-12f ? amax : 1e-12f) / 448.0f;
+            a_s[m * G + g] = s;
+            for (int64_t i = k0; i < k1; ++i) {
+                float v = bf16_value(x[m * K + i]) / s;
+                if (v > 448.0f) v = 448.0f;
+                if (v < -448.0f) v = -448.0f;
+                q[m * K + i] = (uint8_t)fp8bg_oracle_e4m3_encode((double)v);
+            }
+        }
+    }
+}
+
 int fp8bg_oracle_threads(void)
 {
 #ifdef _OPENMP

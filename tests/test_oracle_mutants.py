@@ -2,7 +2,7 @@
 
 Each case plants one mistake in a temporary copy of the oracle's C source
 (a dropped term, a wrong index, a wrong sign, a wrong exponent bias, the
-wrong tie rule), builds it with gcc, swaps it in for the real library and
+wrong tie rule, a wrong scale constant or a missing floor), builds it with gcc, swaps it in for the real library and
 checks that at least one pin test fails.  Everything runs on the CPU.
 """
 import os
@@ -14,6 +14,7 @@ import pytest
 import oracle
 from tests import test_oracle_decode_round as T1
 from tests import test_oracle_gemm as T2
+from tests import test_oracle_quantize as T3
 from tests._cases import golden_cases
 
 MUTANTS = {
@@ -27,6 +28,13 @@ MUTANTS = {
     "ties_away_from_zero": ("nearbyint(x / q)", "round(x / q)"),
     "bf16_precision": ("round_to_format(v, 8, -126, 127)", "round_to_format(v, 9, -126, 127)"),
     "fp16_exponent_bias": ("(unsigned)(E + 15) << 10", "(unsigned)(E + 14) << 10"),
+    "encode_ties_away_from_zero": ("nearbyint(ldexp(a, 3 - e))", "round(ldexp(a, 3 - e))"),
+    "encode_subnormal_boundary": ("if (a < ldexp(1.0, -6)) {", "if (a < ldexp(1.0, -7)) {"),
+    "encode_sign_dropped": ("    return sign | code;\n}", "    return code;\n}"),
+    "quantize_scale_447": ("/ 448.0f;", "/ 447.0f;"),
+    "quantize_no_floor": ("(amax > 1e-12f ? amax : 1e-12f)", "amax"),
+    "quantize_signed_amax": ("fabsf(bf16_value(x[m * K + i]))", "bf16_value(x[m * K + i])"),
+    "quantize_scale_group0": ("a_s[m * G + g] = s;", "a_s[m * G] = s;"),
 }
 
 PINS = [
@@ -43,6 +51,13 @@ PINS = [
     lambda: T2.test_matches_numpy_blas_of_dequantised_operands(37, 300, 512),
     T2.test_identity_weight_exposes_every_code,
     T2.test_row_and_column_block_locality,
+    T3.test_encode_inverts_decode_on_every_finite_code,
+    T3.test_midpoints_round_to_even_code,
+    T3.test_saturation_at_448,
+    T3.test_quantize_constant_group_maps_to_448,
+    T3.test_quantize_zero_groups_keep_sign_and_floor,
+    T3.test_quantize_groups_and_scales_are_per_row_and_per_128,
+    T3.test_dequantised_within_half_a_step,
 ]
 
 
