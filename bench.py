@@ -20,6 +20,8 @@ CPU oracle timed on a bounded sample of the same workload.
 Other modes (for profiles):
   --sweep FILE        every workload and sweep point, one JSON line each, to FILE
   --copy-bytes B      only a plain device copy of B bytes (calibrates HBM counters)
+  --op quantize       time the per-token 1x128 activation quantiser (bf16 -> E4M3
+                      codes + fp32 scales) on the workload's A shape instead
   --no-graph          launch each step eagerly (for counter collection)
 """
 import argparse
@@ -86,29 +88,10 @@ def make_device_copies(w, M, copies, torch, W):
     return d, sets
 
 
-def run_workload(args, w, M, out_name, torch, fbg, W, steps, warmup, use_graph=True,
-                 variant="auto", split_k=0, cfg=None):
-    out_dtype = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[out_name]
-    out_bytes = 4 if out_name == "fp32" else 2
-    N, K = w.N, w.K
-    per_copy = M * K + N * K + 4 * M * (K // 128) + 4 * ((N + 127) // 128) * (K // 128) + M * N * out_bytes
-    copies = max(1, min(args.max_copies, -(-2 * MALL_BYTES // per_copy)))
-    d, sets = make_device_copies(w, M, copies, torch, W)
-    outs = [torch.empty((M, N), dtype=out_dtype, device="cuda:0") for _ in range(copies)]
-    if cfg is not None:
-        os.environ["FBG_FORCE_CONFIG"] = str(cfg)
-    plan = fbg.plan(M, N, K, out_dtype, torch.cuda.get_device_properties(0).multi_processor_count,
-                    variant, split_k)
-    if cfg is not None:
-        plan["config"] = cfg
-    ws = torch.zeros(max(fbg.workspace_size(M, N, K, variant, split_k), 16), dtype=torch.uint8, device="cuda:0")
-    stream = torch.cuda.Stream()
-
-    def step(i):
-        s = sets[i % copies]
-        fbg.gemm(s["A"], s["a_s"], s["B"], s["b_s"], out_dtype=out_dtype, out=outs[i % copies],
-                 workspace=ws, stream=stream, variant=variant, split_k=split_k)
-
+def time_steps(step, copies, steps, warmup, use_graph, stream, torch):
+    """Runs `warmup` untimed steps, then times exactly `steps` steps with HIP
+    events on `stream` (replayed from HIP graphs of one pass over the input
+    copies unless use_graph is false).  Returns (GPU ms, wall seconds)."""
     with torch.cuda.stream(stream):
         for i in range(warmup):
             step(i)
@@ -147,7 +130,33 @@ def run_workload(args, w, M, out_name, torch, fbg, W, steps, warmup, use_graph=T
         ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
+    return ev0.elapsed_time(ev1), wall
+
+
+def run_workload(args, w, M, out_name, torch, fbg, W, steps, warmup, use_graph=True,
+                 variant="auto", split_k=0, cfg=None):
+    out_dtype = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[out_name]
+    out_bytes = 4 if out_name == "fp32" else 2
+    N, K = w.N, w.K
+    per_copy = M * K + N * K + 4 * M * (K // 128) + 4 * ((N + 127) // 128) * (K // 128) + M * N * out_bytes
+    copies = max(1, min(args.max_copies, -(-2 * MALL_BYTES // per_copy)))
+    d, sets = make_device_copies(w, M, copies, torch, W)
+    outs = [torch.empty((M, N), dtype=out_dtype, device="cuda:0") for _ in range(copies)]
+    if cfg is not None:
+        os.environ["FBG_FORCE_CONFIG"] = str(cfg)
+    plan = fbg.plan(M, N, K, out_dtype, torch.cuda.get_device_properties(0).multi_processor_count,
+                    variant, split_k)
+    if cfg is not None:
+        plan["config"] = cfg
+    ws = torch.zeros(max(fbg.workspace_size(M, N, K, variant, split_k), 16), dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.Stream()
+
+    def step(i):
+        s = sets[i % copies]
+        fbg.gemm(s["A"], s["a_s"], s["B"], s["b_s"], out_dtype=out_dtype, out=outs[i % copies],
+                 workspace=ws, stream=stream, variant=variant, split_k=split_k)
+
+    gpu_ms, wall = time_steps(step, copies, steps, warmup, use_graph, stream, torch)
     ms_per_step = gpu_ms / steps
     flops = 2 * M * N * K
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -164,6 +173,63 @@ def run_workload(args, w, M, out_name, torch, fbg, W, steps, warmup, use_graph=T
         os.environ.pop("FBG_FORCE_CONFIG", None)
     return {"d": d, "plan": plan, "ms_per_step": ms_per_step, "tflops": tflops, "gbs": gbs, "roof": roof,
             "copies": copies, "wall_s": wall, "alg_bytes": nbytes}
+
+
+def quantize_bytes(M, K):
+    """Algorithmic bytes of the activation quantiser: bf16 x read once, E4M3 A
+    and fp32 a_s written once."""
+    return 2 * M * K + M * K + 4 * M * (K // 128)
+
+
+def activation_bits(M, K, seed, outlier_frac, np):
+    """Seeded bf16 activations of the workload recipe (N(0,1), outlier rows x10)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=(M, K)).astype(np.float32)
+    if outlier_frac:
+        x[rng.random(M) < outlier_frac] *= 10.0
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def run_quantize(args, w, M, torch, fbg, steps, warmup, use_graph=True):
+    import numpy as np
+    K = w.K
+    bits = activation_bits(M, K, w.seed, w.outlier_frac, np)
+    nbytes = quantize_bytes(M, K)
+    copies = max(1, min(args.max_copies, -(-2 * MALL_BYTES // nbytes)))
+    dev = torch.device("cuda:0")
+    x0 = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    As = [torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev) for _ in range(copies)]
+    ss = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(copies)]
+    stream = torch.cuda.Stream()
+
+    def step(i):
+        j = i % copies
+        fbg.quantize_rows(xs[j], As[j], ss[j], stream=stream)
+
+    gpu_ms, wall = time_steps(step, copies, steps, warmup, use_graph, stream, torch)
+    ms = gpu_ms / steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return {"bits": bits, "ms_per_step": ms, "gbs": gbs, "roof": roof, "copies": copies, "alg_bytes": nbytes}
+
+
+def cpu_baseline_quantize(bits, budget_s=12.0):
+    """The oracle's row quantiser, on the host's cores, over the full input
+    repeated until about `budget_s` have passed."""
+    import oracle
+    reps, t0 = 0, time.perf_counter()
+    nbytes = quantize_bytes(*bits.shape)
+    while True:
+        oracle.quantize_rows(bits)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    return {"value": round(reps * nbytes / el / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle", "sample": f"full activation matrix quantised {reps}x in {el:.1f} s"}
 
 
 def cpu_baseline(d, flops_per_call, budget_s=12.0):
@@ -209,6 +275,8 @@ def main():
     ap.add_argument("--variant", default="auto", help="force a kernel variant (tuning)")
     ap.add_argument("--split", type=int, default=0, help="force a split-K count (tuning)")
     ap.add_argument("--cfg", type=int, default=None, help="force a tile configuration (tuning)")
+    ap.add_argument("--op", default="gemm", choices=["gemm", "quantize"],
+                    help="gemm (default), or the activation quantiser on the workload's A shape")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -242,10 +310,33 @@ def main():
                         f.write(json.dumps(line) + "\n")
                         f.flush()
                         print(json.dumps(line), flush=True)
+            for name, w in W.WORKLOADS.items():     # the activation quantiser on each workload's A
+                r = run_quantize(args, w, w.M, torch, fbg, 200 if w.M * w.K > 1e7 else 2048, 20, not args.no_graph)
+                line = {"op": "quantize", "workload": name, "M": w.M, "K": w.K,
+                        "us": round(r["ms_per_step"] * 1e3, 3), "gbs": round(r["gbs"], 1),
+                        "roofline": r["roof"], "copies": r["copies"]}
+                f.write(json.dumps(line) + "\n")
+                f.flush()
+                print(json.dumps(line), flush=True)
         return
 
     w = W.WORKLOADS[args.workload]
     M = args.M if args.M is not None else w.M
+    if args.op == "quantize":
+        r = run_quantize(args, w, M, torch, fbg, args.steps, args.warmup, not args.no_graph)
+        line = {
+            "metric": "HBM GB/s and % of roofline of the per-token 1x128 activation quantiser, 1\u00d7MI355X",
+            "value": round(r["gbs"], 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 6), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16->e4m3", "data": "synthetic",
+            "config": {"workload": f"quantize_{M}x{w.K}", "M": M, "K": w.K, "input_copies": r["copies"],
+                       "graphs": not args.no_graph},
+            "roofline": dict(r["roof"], traffic=None),
+        }
+        if not args.no_cpu:
+            line["cpu_baseline"] = cpu_baseline_quantize(r["bits"])
+        print(json.dumps(line), flush=True)
+        return
     out = args.out or w.out_dtypes[0]
     r = run_workload(args, w, M, out, torch, fbg, W, args.steps, args.warmup, not args.no_graph,
                      args.variant, args.split, args.cfg)

@@ -61,6 +61,8 @@ def load():
     lib.fp8_block_gemm_plan.argtypes = [_i64, _i64, _i64, _int, _int, _int, _int, ctypes.POINTER(Plan)]
     lib.fp8_block_gemm_status_string.restype = ctypes.c_char_p
     lib.fp8_block_gemm_status_string.argtypes = [_int]
+    lib.fp8_block_gemm_quantize_rows.restype = _int
+    lib.fp8_block_gemm_quantize_rows.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
     lib.fp8_block_gemm_version.restype = _int
     lib.fp8_block_gemm_version.argtypes = []
     _lib = lib
@@ -150,3 +152,30 @@ def gemm(A: torch.Tensor, a_s: torch.Tensor, B: torch.Tensor, b_s: torch.Tensor,
     if st != SUCCESS:
         raise FP8BGError(st, "fp8_block_gemm")
     return out
+
+
+def quantize_rows(x: torch.Tensor, A: torch.Tensor = None, a_s: torch.Tensor = None,
+                  stream: torch.cuda.Stream = None):
+    """Per-token 1x128 quantisation of bf16 activations x [M,K] into E4M3 codes
+    A [M,K] (float8_e4m3fn) and fp32 scales a_s [M, K/128], on the current
+    stream (or `stream`): a_s = max(amax, 1e-12)/448 per 128-wide group,
+    A = E4M3_RNE(clamp(x / a_s, +-448)).  See fp8_block_gemm_quantize_rows in
+    include/fp8bg.h."""
+    lib = load()
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x must be a contiguous 2-D bfloat16 CUDA tensor")
+    M, K = x.shape
+    G = (K + 127) // 128
+    if A is None:
+        A = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=x.device)
+    else:
+        _check(A, "A", FP8_DTYPES, (M, K), x.device)
+    if a_s is None:
+        a_s = torch.empty((M, G), dtype=torch.float32, device=x.device)
+    else:
+        _check(a_s, "a_s", (torch.float32,), (M, G), x.device)
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    st = lib.fp8_block_gemm_quantize_rows(x.data_ptr(), M, K, A.data_ptr(), a_s.data_ptr(), s.cuda_stream)
+    if st != SUCCESS:
+        raise FP8BGError(st, "fp8_block_gemm_quantize_rows")
+    return A, a_s

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8bg.so")
-SOURCES = ["fp8bg_api.hip", "fp8bg_kernels.hip", "fp8bg_plan.cpp"]
+SOURCES = ["fp8bg_api.hip", "fp8bg_kernels.hip", "fp8bg_quant.hip", "fp8bg_plan.cpp"]
 ARCH = "gfx950"
 
 

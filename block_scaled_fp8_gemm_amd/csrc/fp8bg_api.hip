@@ -188,3 +188,19 @@ extern "C" size_t fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K,
     return (size_t)-1;
   return (size_t)p.workspace_bytes;
 }
+
+extern "C" int fp8_block_gemm_quantize_rows(const void* x, int64_t M, int64_t K, void* A, float* a_s, void* stream_) {
+  if (M < 0 || K < 0) return FBG_ERROR_INVALID_VALUE;
+  if (K % 128 != 0) return FBG_ERROR_UNSUPPORTED;
+  if (M > INT32_MAX || K > INT32_MAX) return FBG_ERROR_UNSUPPORTED;
+  const int64_t G = K / 128, bytesX = M * K * 2, bytesA = M * K, bytesAs = M * G * 4;
+  if ((bytesX > 0 && !x) || (bytesA > 0 && !A) || (bytesAs > 0 && !a_s)) return FBG_ERROR_INVALID_VALUE;
+  if (overlaps(A, bytesA, x, bytesX) || overlaps(a_s, bytesAs, x, bytesX) || overlaps(A, bytesA, a_s, bytesAs))
+    return FBG_ERROR_INVALID_VALUE;
+  if ((bytesX > 0 && !aligned(x, 16)) || (bytesA > 0 && !aligned(A, 8)) || (bytesAs > 0 && !aligned(a_s, 4)))
+    return FBG_ERROR_UNSUPPORTED;
+  if (M == 0 || K == 0) return FBG_SUCCESS;
+  const hipError_t e = fbg::launch_quantize_rows(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(A), a_s,
+                                                 M * G, static_cast<hipStream_t>(stream_));
+  return e == hipSuccess ? FBG_SUCCESS : FBG_ERROR_HIP;
+}

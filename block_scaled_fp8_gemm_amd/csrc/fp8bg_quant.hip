@@ -1,0 +1,102 @@
+// gfx950 kernel of the per-token 1x128 activation quantiser, the producer of
+// the GEMM's A and a_s:  bf16 x [M,K]  ->  OCP E4M3 codes A [M,K] and fp32
+// scales a_s [M, K/128].  (FlagGems-vllm PR #693, "feat: optimize w8a8 block
+// fp8 matmul for Hopper", section "Description": per-token FP8 E4M3
+// activations with de-quant scales.)
+//
+//   a_s[m,g] = max(max_{k in group g} |x[m,k]|, 1e-12) / 448
+//   A[m,k]   = E4M3 round-to-nearest-even of clamp(x[m,k] / a_s[m,g], -448, 448)
+//
+// 448 is E4M3's largest finite value.  The scale is an IEEE fp32 division;
+// the codes are those of the IEEE fp32 quotients x / a_s.  The quotient is
+// formed as y = 1/a_s (one correctly rounded division per group), q = x*y,
+// then one correction step q' = fma(fma(-q, a_s, x), y, q) (Markstein's),
+// with x's sign: 3 VALU operations instead of a full division per element
+// (the division sequence took a fifth of the kernel's time).  For every
+// possible pair of a bf16 x and a bf16 group maximum (about 1.07e9 pairs)
+// q' has the same E4M3 code as x / a_s; the quotients differ only below
+// 2^-80, where both codes are zero of x's sign.
+//
+// HBM-bound: 2 bytes read and 1 byte written per element, 4 bytes per
+// 128-wide group.  With K % 128 == 0 the groups are contiguous in memory, so
+// the matrix is a flat run of M*K/128 groups; a wave takes kQuads runs of 4
+// consecutive groups (16 lanes per group, 8 elements = one 16-byte load per
+// lane), issues every load before any arithmetic, and writes 8 codes per lane
+// with one 8-byte store.  The group maximum is a 16-lane butterfly.
+#include "fp8bg_internal.h"
+
+namespace fbg {
+
+namespace {
+
+constexpr int kQuads = 2;  // 4-group runs per wave
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+// Four fp32 values -> four E4M3 codes in one dword (byte i = value i), by the
+// gfx950 conversion instruction (OCP E4M3, round to nearest even).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
+                                                       float* __restrict__ a_s, int64_t groups) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane >> 4, part = lane & 15;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  uint4 raw[kQuads];
+#pragma unroll
+  for (int u = 0; u < kQuads; ++u) {
+    const int64_t g = (wave * kQuads + u) * 4 + sub;
+    raw[u] = g < groups ? *reinterpret_cast<const uint4*>(x + g * 128 + part * 8) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < kQuads; ++u) {
+    const int64_t g = (wave * kQuads + u) * 4 + sub;
+    const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    // Maximum over the group's 16 lanes (lanes 16*sub .. 16*sub + 15).
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    const float s = fmaxf(amax, 1e-12f) / 448.0f;
+    const float y = 1.0f / s;
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float t = v[i] * y;
+      const float e = __builtin_fmaf(-t, s, v[i]);
+      r[i] = clamp448(__builtin_copysignf(__builtin_fmaf(e, y, t), v[i]));
+    }
+    if (g < groups) {
+      *reinterpret_cast<uint2*>(q + g * 128 + part * 8) =
+          make_uint2(e4m3x4(r[0], r[1], r[2], r[3]), e4m3x4(r[4], r[5], r[6], r[7]));
+      if (part == 0) a_s[g] = s;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* q, float* a_s, int64_t groups, hipStream_t stream) {
+  const int64_t waves = (groups + 4 * kQuads - 1) / (4 * kQuads);
+  const int64_t blocks = (waves + 3) / 4;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)blocks), dim3(256), 0, stream, x, q, a_s, groups);
+  return hipGetLastError();
+}
+
+}  // namespace fbg

@@ -129,6 +129,28 @@ size_t fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int varian
 int fp8_block_gemm_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count,
                         int variant, int split_k, fbg_plan *out);
 
+/*
+ * fp8_block_gemm_quantize_rows -- the producer of A and a_s: per-token 1x128
+ * quantisation of bf16 activations to OCP E4M3 (the section "Description"
+ * gives the GEMM per-token FP8 E4M3 activations with one de-quant scale per
+ * 128-wide K group; the scale maps each group's largest magnitude onto
+ * E4M3's largest finite value, 448).  For every row m and group g:
+ *
+ *     a_s[m,g] = max(max_{k in g} |x[m,k]|, 1e-12f) / 448        (fp32 division)
+ *     A[m,k]   = E4M3 round-to-nearest-even of clamp(x[m,k] / a_s[m,g], -448, 448)
+ *
+ * with x[m,k] / a_s[m,g] an IEEE fp32 (correctly rounded) division.
+ * x: [M,K] bf16, row-major, 16-byte aligned (read); A: [M,K] E4M3 bytes,
+ * 8-byte aligned, and a_s: [M, K/128] fp32, 4-byte aligned (written in full).
+ * The caller owns all three; outputs must not overlap x or each other.
+ * M, K >= 0 with K % 128 == 0; M == 0 or K == 0: success, nothing launched.
+ * A null pointer with a non-empty extent, a negative size or overlapping
+ * buffers -> INVALID_VALUE; K % 128 != 0 or misalignment -> UNSUPPORTED.
+ * NaN or infinite inputs are outside the contract.  Asynchronous on
+ * `stream`; deterministic.
+ */
+int fp8_block_gemm_quantize_rows(const void *x, int64_t M, int64_t K, void *A, float *a_s, void *stream);
+
 /* fp8_block_gemm_status_string -- static text for a status code. */
 const char *fp8_block_gemm_status_string(int status);
 

@@ -165,3 +165,31 @@ def test_every_tile_configuration_has_parity_cases():
     assert ids("FBG_GENERIC_CFGS") <= have["generic"]
     assert ids("FBG_SWAP_CFGS") <= have["swap_ab"]
     assert ids("FBG_SHORT_CFGS") <= have["short_k256"]
+
+
+def _qcall(x=0x100000, M=4, K=256, A=0x200000, a_s=0x300000):
+    return fbg.load().fp8_block_gemm_quantize_rows(x, M, K, A, a_s, None)
+
+
+def test_quantize_host_validation_statuses():
+    # As above: every case fails validation (or is empty) before any HIP call.
+    assert _qcall(x=None) == fbg.INVALID_VALUE
+    assert _qcall(A=None) == fbg.INVALID_VALUE
+    assert _qcall(a_s=None) == fbg.INVALID_VALUE
+    assert _qcall(M=-1) == fbg.INVALID_VALUE
+    assert _qcall(K=-128) == fbg.INVALID_VALUE
+    assert _qcall(K=200) == fbg.UNSUPPORTED
+    assert _qcall(x=0x100008) == fbg.UNSUPPORTED           # x not 16-byte aligned
+    assert _qcall(A=0x200004) == fbg.UNSUPPORTED           # A not 8-byte aligned
+    assert _qcall(a_s=0x300002) == fbg.UNSUPPORTED
+    assert _qcall(A=0x100000 + 512) == fbg.INVALID_VALUE   # A overlaps x (x is 4*256*2 bytes)
+    assert _qcall(a_s=0x200000 + 8) == fbg.INVALID_VALUE   # a_s overlaps A
+    assert _qcall(M=0, x=None, A=None, a_s=None) == fbg.SUCCESS
+    assert _qcall(K=0, x=None, A=None, a_s=None) == fbg.SUCCESS
+
+
+def test_quantize_wrapper_checks():
+    with pytest.raises(ValueError):
+        fbg.quantize_rows(torch.zeros(4, 128, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        fbg.quantize_rows(torch.zeros(4, 128, dtype=torch.bfloat16))      # not on a GPU

@@ -1,0 +1,134 @@
+"""GPU parity of the activation quantiser (fp8_block_gemm_quantize_rows,
+through the C ABI) with the CPU oracle: E4M3 codes and fp32 scales bit for
+bit.  Floating point decides an integer code here, so both sides take the
+decision from the same IEEE fp32 quotient x / a_s.
+
+Recipe: FlagGems-vllm PR #693, "feat: optimize w8a8 block fp8 matmul for
+Hopper", section "Description" (per-token FP8 E4M3 activations with
+de-quant scales); a_s = max(amax, 1e-12)/448 per 128-wide group.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_gemm_amd as fbg
+import oracle
+import workloads
+from tests._gpu import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def run_q(bits: np.ndarray):
+    x = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    A, a_s = fbg.quantize_rows(x)
+    torch.cuda.synchronize()
+    return A.view(torch.uint8).cpu().numpy(), a_s.cpu().numpy()
+
+
+def assert_same(bits, what):
+    q, s = run_q(bits)
+    qr, sr = oracle.quantize_rows(bits)
+    bad_s = np.argwhere(s.view(np.uint32) != sr.view(np.uint32))
+    assert bad_s.size == 0, f"{what}: scales differ at {bad_s[:4].tolist()}: {s[tuple(bad_s[0])]} vs {sr[tuple(bad_s[0])]}"
+    bad = np.argwhere(q != qr)
+    if bad.size:
+        m, k = bad[0]
+        v = float(bf16_to_f32(bits[m:m + 1, k:k + 1])[0, 0])
+        pytest.fail(f"{what}: {len(bad)} codes differ, first at ({m},{k}): x={v!r} "
+                    f"gpu={q[m, k]:#04x} oracle={qr[m, k]:#04x}")
+
+
+def test_every_bf16_in_range_with_unit_scale(gpu):
+    """Groups led by a 448 element have a_s = 448/448 = 1 exactly, so every
+    code is the E4M3 rounding of the bf16 value itself: all of them."""
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = bf16_to_f32(allb)
+    vals = allb[np.isfinite(v) & (np.abs(v) <= 448.0)]
+    per = 127
+    ngroups = -(-len(vals) // per)
+    g = np.zeros((ngroups, 128), dtype=np.uint16)
+    g[:, 0] = bf16_bits(np.array([448.0], np.float32))[0]
+    flat = np.zeros(ngroups * per, dtype=np.uint16)
+    flat[:len(vals)] = vals
+    g[:, 1:] = flat.reshape(ngroups, per)
+    gpr = 8                                    # groups per row: K = 1024
+    rows = -(-ngroups // gpr)
+    pad = np.zeros((rows * gpr - ngroups, 128), dtype=np.uint16)
+    pad[:, 0] = g[0, 0]
+    bits = np.concatenate([g, pad]).reshape(rows, gpr * 128)
+    _, s = run_q(bits)
+    assert np.all(s == 1.0)
+    assert_same(bits, "all bf16 values")
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 384), (5, 256), (17, 1024), (65, 4096), (130, 640)])
+def test_random_rows(gpu, M, K):
+    rng = np.random.default_rng(M * 1000 + K)
+    x = rng.normal(size=(M, K)).astype(np.float32) * np.exp(rng.normal(size=(M, 1)) * 4).astype(np.float32)
+    G = K // 128
+    if M > 2:
+        x[1, :128] = 0.0                       # all-zero group: the 1e-12 floor
+        x[2, :] *= 1e4                         # outlier row
+    if M > 4 and G > 1:
+        x[4, 128:256] = -0.0                   # negative zeros keep their sign
+        x[3, 256 % K:256 % K + 128] *= 1e-30   # tiny values, codes underflow to zero
+    assert_same(bf16_bits(x), f"random {M}x{K}")
+
+
+def test_prefill_size_sampled_rows(gpu):
+    """At the prefill activation size (16384 x 4096, 1% outlier rows x10),
+    with the launch the benchmark times: rows every 64th and every outlier row
+    checked against the oracle (the quantisation is row-local)."""
+    M, K = 16384, 4096
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=(M, K)).astype(np.float32)
+    out_rows = np.nonzero(rng.random(M) < 0.01)[0]
+    x[out_rows] *= 10.0
+    bits = bf16_bits(x)
+    q, s = run_q(bits)
+    rows = np.union1d(np.arange(0, M, 64), out_rows)
+    qr, sr = oracle.quantize_rows(bits[rows])
+    assert np.array_equal(s[rows].view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(q[rows], qr)
+
+
+def test_deterministic_and_empty(gpu):
+    rng = np.random.default_rng(1)
+    bits = bf16_bits(rng.normal(size=(33, 512)).astype(np.float32))
+    q1, s1 = run_q(bits)
+    q2, s2 = run_q(bits)
+    assert np.array_equal(q1, q2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    A, a_s = fbg.quantize_rows(torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda:0"))
+    assert A.shape == (0, 256) and a_s.shape == (0, 2)
+    with pytest.raises(fbg.FP8BGError) as e:
+        fbg.quantize_rows(torch.zeros((4, 200), dtype=torch.bfloat16, device="cuda:0"))
+    assert e.value.status == fbg.UNSUPPORTED
+
+
+def test_quantised_activations_feed_the_gemm(gpu):
+    """End to end: the GPU-quantised A and a_s are the oracle's bit for bit,
+    so the GEMM on them equals the GEMM on the oracle's, bit for bit."""
+    M, N, K = 96, 384, 1024
+    rng = np.random.default_rng(9)
+    bits = bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+    d = workloads.make_inputs(M, N, K, seed=9)
+    B, b_s = to_dev(d)["B"], to_dev(d)["b_s"]
+    x = torch.from_numpy(bits.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    A, a_s = fbg.quantize_rows(x)
+    qr, sr = oracle.quantize_rows(bits)
+    Ar = torch.from_numpy(qr).to("cuda:0").view(torch.float8_e4m3fn)
+    sr_t = torch.from_numpy(sr).to("cuda:0")
+    C1 = fbg.gemm(A, a_s, B, b_s)
+    C2 = fbg.gemm(Ar, sr_t, B, b_s)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
