@@ -54,6 +54,9 @@ def _load():
     lib.fp8bg_oracle_quantize_rows.restype = None
     lib.fp8bg_oracle_quantize_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_void_p, ctypes.c_void_p]
+    lib.fp8bg_oracle_quantize_blocks.restype = None
+    lib.fp8bg_oracle_quantize_blocks.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                                 ctypes.c_void_p, ctypes.c_void_p]
     lib.fp8bg_oracle_threads.restype = ctypes.c_int
     lib.fp8bg_oracle_threads.argtypes = []
     _lib = lib
@@ -172,3 +175,23 @@ def quantize_rows(x_bf16_bits):
     if M and K:
         _load().fp8bg_oracle_quantize_rows(x.ctypes.data, M, K, q.ctypes.data, a_s.ctypes.data)
     return q, a_s
+
+
+def quantize_blocks(w_bf16_bits):
+    """128 x 128 block quantisation of bf16 weights (FlagGems-vllm PR #693,
+    section "Description": FP8 E4M3 weights with [block_n, block_k] = [128, 128]
+    de-quant scales).
+
+    w_bf16_bits: uint16 [N,K] bf16 bit patterns.  Returns (B, b_s): uint8 [N,K]
+    E4M3 codes and float32 [ceil(N/128), ceil(K/128)] scales, with
+    b_s = max(amax, 1e-12)/448 per block and B = E4M3_RNE(clamp(w/b_s, +-448)),
+    both divisions in fp32.
+    """
+    w = np.ascontiguousarray(w_bf16_bits, dtype=np.uint16)
+    N, K = w.shape
+    NB, G = (N + GROUP - 1) // GROUP, (K + GROUP - 1) // GROUP
+    q = np.empty((N, K), dtype=np.uint8)
+    b_s = np.empty((NB, G), dtype=np.float32)
+    if N and K:
+        _load().fp8bg_oracle_quantize_blocks(w.ctypes.data, N, K, q.ctypes.data, b_s.ctypes.data)
+    return q, b_s

@@ -30,9 +30,10 @@
  * The cast to the output dtype is one IEEE round-to-nearest-even step from
  * the fp64 value (the pages only say "casts"; RNE is the reading taken).
  *
- * It also computes the producer of A and a_s, the per-token 1 x 128
- * activation quantisation (fp8bg_oracle_quantize_rows, with the E4M3
- * encoder fp8bg_oracle_e4m3_encode written from the format definition).
+ * It also computes the producers of the operands: the per-token 1 x 128
+ * activation quantisation (fp8bg_oracle_quantize_rows) and the 128 x 128
+ * weight-block quantisation (fp8bg_oracle_quantize_blocks), with the E4M3
+ * encoder fp8bg_oracle_e4m3_encode written from the format definition.
  */
 #include <math.h>
 #include <stdint.h>
@@ -252,6 +253,50 @@ void fp8bg_oracle_quantize_rows(const uint16_t *x, int64_t M, int64_t K,
                 if (v < -448.0f) v = -448.0f;
                 q[m * K + i] = (uint8_t)fp8bg_oracle_e4m3_encode((double)v);
             }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Weight quantisation to E4M3 with one fp32 scale per 128 x 128 block: the */
+/* producer of B and b_s (the pages' [block_n, block_k] = [128, 128] weight */
+/* de-quant scales, FlagGems-vllm PR #693, section "Description").          */
+/*                                                                          */
+/*     amax    = max over the block's rows n and columns k of |w[n,k]|      */
+/*     b_s     = max(amax, 1e-12f) / 448                 (fp32 division)    */
+/*     B[n,k]  = E4M3_RNE(clamp(w[n,k] / b_s, -448, 448))  (fp32 division)  */
+/*                                                                          */
+/* The last block row holds the N % 128 remaining rows when N is not a      */
+/* multiple of 128 (b_s has ceil(N/128) rows).                               */
+/* ------------------------------------------------------------------------ */
+
+/* w: [N,K] bf16 bit patterns, row-major; q: [N,K] codes; b_s: [ceil(N/128), ceil(K/128)]. */
+void fp8bg_oracle_quantize_blocks(const uint16_t *w, int64_t N, int64_t K,
+                                  uint8_t *q, float *b_s)
+{
+    const int64_t NB = (N + ORACLE_GROUP - 1) / ORACLE_GROUP;
+    const int64_t G = (K + ORACLE_GROUP - 1) / ORACLE_GROUP;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t bn = 0; bn < NB; ++bn) {
+        for (int64_t g = 0; g < G; ++g) {
+            const int64_t n0 = bn * ORACLE_GROUP, n1 = n0 + ORACLE_GROUP < N ? n0 + ORACLE_GROUP : N;
+            const int64_t c0 = g * ORACLE_GROUP, c1 = c0 + ORACLE_GROUP < K ? c0 + ORACLE_GROUP : K;
+            float amax = 0.0f;
+            for (int64_t n = n0; n < n1; ++n)
+                for (int64_t c = c0; c < c1; ++c) {
+                    const float v = fabsf(bf16_value(w[n * K + c]));
+                    if (v > amax)
+                        amax = v;
+                }
+            const float s = (amax > 1e-12f ? amax : 1e-12f) / 448.0f;
+            b_s[bn * G + g] = s;
+            for (int64_t n = n0; n < n1; ++n)
+                for (int64_t c = c0; c < c1; ++c) {
+                    float v = bf16_value(w[n * K + c]) / s;
+                    if (v > 448.0f) v = 448.0f;
+                    if (v < -448.0f) v = -448.0f;
+                    q[n * K + c] = (uint8_t)fp8bg_oracle_e4m3_encode((double)v);
+                }
         }
     }
 }

@@ -31,10 +31,18 @@ MUTANTS = {
     "encode_ties_away_from_zero": ("nearbyint(ldexp(a, 3 - e))", "round(ldexp(a, 3 - e))"),
     "encode_subnormal_boundary": ("if (a < ldexp(1.0, -6)) {", "if (a < ldexp(1.0, -7)) {"),
     "encode_sign_dropped": ("    return sign | code;\n}", "    return code;\n}"),
-    "quantize_scale_447": ("/ 448.0f;", "/ 447.0f;"),
-    "quantize_no_floor": ("(amax > 1e-12f ? amax : 1e-12f)", "amax"),
+    "quantize_scale_447": ("(amax > 1e-12f ? amax : 1e-12f) / 448.0f;\n            a_s[",
+                           "(amax > 1e-12f ? amax : 1e-12f) / 447.0f;\n            a_s["),
+    "quantize_no_floor": ("(amax > 1e-12f ? amax : 1e-12f) / 448.0f;\n            a_s[", "amax / 448.0f;\n            a_s["),
+    "blocks_scale_447": ("(amax > 1e-12f ? amax : 1e-12f) / 448.0f;\n            b_s[",
+                         "(amax > 1e-12f ? amax : 1e-12f) / 447.0f;\n            b_s["),
     "quantize_signed_amax": ("fabsf(bf16_value(x[m * K + i]))", "bf16_value(x[m * K + i])"),
     "quantize_scale_group0": ("a_s[m * G + g] = s;", "a_s[m * G] = s;"),
+    "blocks_scale_row0": ("b_s[bn * G + g] = s;", "b_s[g] = s;"),
+    "blocks_ragged_rows_dropped": ("n1 = n0 + ORACLE_GROUP < N ? n0 + ORACLE_GROUP : N;",
+                                   "n1 = n0 + ORACLE_GROUP < N ? n0 + ORACLE_GROUP : n0 + (N - n0) / 2;"),
+    "blocks_amax_one_row": ("for (int64_t n = n0; n < n1; ++n)\n                for (int64_t c = c0; c < c1; ++c) {\n                    const float v = fabsf",
+                            "for (int64_t n = n0; n < n0 + 1; ++n)\n                for (int64_t c = c0; c < c1; ++c) {\n                    const float v = fabsf"),
 }
 
 PINS = [
@@ -58,6 +66,10 @@ PINS = [
     T3.test_quantize_zero_groups_keep_sign_and_floor,
     T3.test_quantize_groups_and_scales_are_per_row_and_per_128,
     T3.test_dequantised_within_half_a_step,
+    T3.test_blocks_constant_block_maps_to_448,
+    T3.test_blocks_scale_is_local_to_its_block,
+    T3.test_blocks_ragged_last_block_row,
+    T3.test_blocks_dequantised_within_half_a_step,
 ]
 
 

@@ -1,5 +1,6 @@
-"""Pins of the oracle's activation quantiser (E4M3 encoder + per-token 1x128
-row quantisation) against what the format and the definition fix:
+"""Pins of the oracle's quantisers (the E4M3 encoder, per-token 1x128 row
+quantisation of activations and 128x128 block quantisation of weights)
+against what the format and the definition fix:
 
 - the encoder inverts the decoder on every finite code (incl. -0);
 - midpoints between neighbouring codes go to the even code, points just off
@@ -9,7 +10,10 @@ row quantisation) against what the format and the definition fix:
   and on random fp32 values;
 - closed forms of the row quantiser: a constant group maps to +-448 with
   a_s = |v|/448, an all-zero group to +-0 with the 1e-12 floor;
-- dequantisation stays within half an E4M3 step of the input.
+- dequantisation stays within half an E4M3 step of the input;
+- weight blocks: a constant block maps to +-448, a block's scale depends on
+  its own 128x128 elements only (ragged last block row included), and the
+  torch-op recipe and the input generator give the same codes and scales.
 
 Quantisation recipe: FlagGems-vllm PR #693, "feat: optimize w8a8 block fp8
 matmul for Hopper", section "Description" (per-token FP8 E4M3 activations
@@ -152,3 +156,75 @@ def test_quantize_matches_torch_recipe(shape):
     qt = torch.clamp(xt / s[..., None], -448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
     assert np.array_equal(a_s, s.numpy())
     assert np.array_equal(q, qt.reshape(shape).numpy())
+
+
+# ---------------------------------------------------------------------------
+# 128 x 128 weight blocks (section "Description": [block_n, block_k] = [128, 128]
+# weight de-quant scales).
+# ---------------------------------------------------------------------------
+def test_blocks_constant_block_maps_to_448():
+    w = np.full((128, 256), -0.02, dtype=np.float32)
+    w[:, 128:] = 3.0
+    q, b_s = oracle.quantize_blocks(bf16_bits(w))
+    v0 = float(bf16_to_f32(bf16_bits(np.array([-0.02], np.float32)))[0])
+    assert b_s.shape == (1, 2)
+    assert b_s[0, 0] == np.float32(abs(v0)) / np.float32(448.0)
+    assert b_s[0, 1] == np.float32(3.0) / np.float32(448.0)
+    assert np.all(q[:, :128] == 0xFE) and np.all(q[:, 128:] == 0x7E)
+
+
+def test_blocks_scale_is_local_to_its_block():
+    rng = np.random.default_rng(4)
+    w = (rng.normal(size=(300, 384)) * 0.02).astype(np.float32)
+    q0, s0 = oracle.quantize_blocks(bf16_bits(w))
+    w2 = w.copy()
+    w2[130, 300] = 5.0                       # block (1, 2) only
+    q1, s1 = oracle.quantize_blocks(bf16_bits(w2))
+    changed = np.argwhere(s0 != s1)
+    assert changed.tolist() == [[1, 2]]
+    diff_rows, diff_cols = np.nonzero(q0 != q1)
+    assert diff_rows.min() >= 128 and diff_rows.max() < 256
+    assert diff_cols.min() >= 256 and diff_cols.max() < 384
+
+
+def test_blocks_ragged_last_block_row():
+    """N = 300: the third block row holds rows 256..299 only; its amax ignores
+    nothing and includes nothing else."""
+    rng = np.random.default_rng(5)
+    w = (rng.normal(size=(300, 128)) * 0.02).astype(np.float32)
+    w[299, 7] = -2.5
+    q, b_s = oracle.quantize_blocks(bf16_bits(w))
+    assert b_s.shape == (3, 1)
+    assert b_s[2, 0] == np.float32(2.5) / np.float32(448.0)
+    assert q[299, 7] == 0xFE
+
+
+def test_blocks_match_torch_recipe_and_generator():
+    """The recipe written with torch ops (block amax, fp32 division, clamp,
+    RNE cast), and the input generator's own weight quantiser, give the same
+    codes and scales."""
+    import workloads
+    rng = np.random.default_rng(6)
+    w = (rng.normal(size=(256, 512)) * 0.02).astype(np.float32)
+    bits = bf16_bits(w)
+    q, b_s = oracle.quantize_blocks(bits)
+    wt = torch.from_numpy(bf16_to_f32(bits)).view(2, 128, 4, 128)
+    s = torch.clamp(wt.abs().amax(dim=(1, 3)), min=float(np.float32(1e-12))) / 448.0
+    qt = torch.clamp(wt / s[:, None, :, None], -448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(b_s, s.numpy())
+    assert np.array_equal(q, qt.reshape(256, 512).numpy())
+    qg, sg = workloads.quantize_blocks(bf16_to_f32(bits))
+    assert np.array_equal(qg, q) and np.array_equal(sg, b_s)
+
+
+def test_blocks_dequantised_within_half_a_step():
+    rng = np.random.default_rng(12)
+    w = (rng.normal(size=(260, 640)) * np.exp(rng.normal(size=(260, 1)))).astype(np.float32)
+    bits = bf16_bits(w)
+    q, b_s = oracle.quantize_blocks(bits)
+    table = oracle.e4m3_table()
+    wb = bf16_to_f32(bits).astype(np.float64)
+    s = np.repeat(np.repeat(b_s.astype(np.float64), 128, axis=0)[:260], 128, axis=1)
+    y = wb / s
+    step = np.where(np.abs(y) < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(y), 1e-300))) - 3))
+    assert np.all(np.abs(table[q] * s - wb) <= (0.5 * step + np.abs(y) * 2.0 ** -23) * s * (1 + 1e-12))
