@@ -22,6 +22,7 @@ Other modes (for profiles):
   --copy-bytes B      only a plain device copy of B bytes (calibrates HBM counters)
   --op quantize       time the per-token 1x128 activation quantiser (bf16 -> E4M3
                       codes + fp32 scales) on the workload's A shape instead
+  --op quantize_weights   the 128x128 weight-block quantiser on the workload's B shape
   --no-graph          launch each step eagerly (for counter collection)
 """
 import argparse
@@ -191,45 +192,60 @@ def activation_bits(M, K, seed, outlier_frac, np):
     return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def run_quantize(args, w, M, torch, fbg, steps, warmup, use_graph=True):
+def run_quantize(args, w, M, torch, fbg, steps, warmup, use_graph=True, weights=False):
+    """Times the activation quantiser on the workload's A [M,K] or, with
+    weights=True, the 128x128 weight quantiser on its B [N,K]."""
     import numpy as np
     K = w.K
-    bits = activation_bits(M, K, w.seed, w.outlier_frac, np)
-    nbytes = quantize_bytes(M, K)
+    if weights:
+        M = w.N
+        rng = np.random.default_rng(w.seed + 1000)
+        wf = (rng.normal(size=(M, K)) * 0.02).astype(np.float32)
+        bits = torch.from_numpy(wf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nbytes = 2 * M * K + M * K + 4 * ((M + 127) // 128) * (K // 128)
+        srows = (M + 127) // 128
+    else:
+        bits = activation_bits(M, K, w.seed, w.outlier_frac, np)
+        nbytes = quantize_bytes(M, K)
+        srows = M
     copies = max(1, min(args.max_copies, -(-2 * MALL_BYTES // nbytes)))
     dev = torch.device("cuda:0")
     x0 = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
     xs = [x0] + [x0.clone() for _ in range(copies - 1)]
     As = [torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev) for _ in range(copies)]
-    ss = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(copies)]
+    ss = [torch.empty((srows, K // 128), dtype=torch.float32, device=dev) for _ in range(copies)]
     stream = torch.cuda.Stream()
+    fn = fbg.quantize_blocks if weights else fbg.quantize_rows
 
     def step(i):
         j = i % copies
-        fbg.quantize_rows(xs[j], As[j], ss[j], stream=stream)
+        fn(xs[j], As[j], ss[j], stream=stream)
 
     gpu_ms, wall = time_steps(step, copies, steps, warmup, use_graph, stream, torch)
     ms = gpu_ms / steps
     gbs = nbytes / (ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    return {"bits": bits, "ms_per_step": ms, "gbs": gbs, "roof": roof, "copies": copies, "alg_bytes": nbytes}
+    return {"bits": bits, "ms_per_step": ms, "gbs": gbs, "roof": roof, "copies": copies, "alg_bytes": nbytes,
+            "rows": M}
 
 
-def cpu_baseline_quantize(bits, budget_s=12.0):
-    """The oracle's row quantiser, on the host's cores, over the full input
-    repeated until about `budget_s` have passed."""
+def cpu_baseline_quantize(bits, budget_s=12.0, weights=False):
+    """The oracle's row (or weight-block) quantiser, on the host's cores, over
+    the full input repeated until about `budget_s` have passed."""
     import oracle
     reps, t0 = 0, time.perf_counter()
-    nbytes = quantize_bytes(*bits.shape)
+    R, K = bits.shape
+    nbytes = 3 * R * K + 4 * ((R + 127) // 128 if weights else R) * (K // 128)
+    fn = oracle.quantize_blocks if weights else oracle.quantize_rows
     while True:
-        oracle.quantize_rows(bits)
+        fn(bits)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 1000:
             break
     return {"value": round(reps * nbytes / el / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
-            "kind": "oracle", "sample": f"full activation matrix quantised {reps}x in {el:.1f} s"}
+            "kind": "oracle", "sample": f"full {'weight' if weights else 'activation'} matrix quantised {reps}x in {el:.1f} s"}
 
 
 def cpu_baseline(d, flops_per_call, budget_s=12.0):
@@ -275,8 +291,9 @@ def main():
     ap.add_argument("--variant", default="auto", help="force a kernel variant (tuning)")
     ap.add_argument("--split", type=int, default=0, help="force a split-K count (tuning)")
     ap.add_argument("--cfg", type=int, default=None, help="force a tile configuration (tuning)")
-    ap.add_argument("--op", default="gemm", choices=["gemm", "quantize"],
-                    help="gemm (default), or the activation quantiser on the workload's A shape")
+    ap.add_argument("--op", default="gemm", choices=["gemm", "quantize", "quantize_weights"],
+                    help="gemm (default), the activation quantiser on the workload's A shape, "
+                         "or the 128x128 weight quantiser on its B shape")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -322,19 +339,23 @@ def main():
 
     w = W.WORKLOADS[args.workload]
     M = args.M if args.M is not None else w.M
-    if args.op == "quantize":
-        r = run_quantize(args, w, M, torch, fbg, args.steps, args.warmup, not args.no_graph)
+    if args.op in ("quantize", "quantize_weights"):
+        wts = args.op == "quantize_weights"
+        r = run_quantize(args, w, M, torch, fbg, args.steps, args.warmup, not args.no_graph, weights=wts)
+        M = r["rows"]
         line = {
-            "metric": "HBM GB/s and % of roofline of the per-token 1x128 activation quantiser, 1\u00d7MI355X",
+            "metric": ("HBM GB/s and % of roofline of the 128x128 weight quantiser, 1\u00d7MI355X" if wts else
+                       "HBM GB/s and % of roofline of the per-token 1x128 activation quantiser, 1\u00d7MI355X"),
             "value": round(r["gbs"], 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 6), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16->e4m3", "data": "synthetic",
-            "config": {"workload": f"quantize_{M}x{w.K}", "M": M, "K": w.K, "input_copies": r["copies"],
+            "config": {"workload": f"{'quantize_weights' if wts else 'quantize'}_{M}x{w.K}", "rows": M, "K": w.K,
+                       "input_copies": r["copies"],
                        "graphs": not args.no_graph},
             "roofline": dict(r["roof"], traffic=None),
         }
         if not args.no_cpu:
-            line["cpu_baseline"] = cpu_baseline_quantize(r["bits"])
+            line["cpu_baseline"] = cpu_baseline_quantize(r["bits"], weights=wts)
         print(json.dumps(line), flush=True)
         return
     out = args.out or w.out_dtypes[0]

@@ -63,6 +63,8 @@ def load():
     lib.fp8_block_gemm_status_string.argtypes = [_int]
     lib.fp8_block_gemm_quantize_rows.restype = _int
     lib.fp8_block_gemm_quantize_rows.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
+    lib.fp8_block_gemm_quantize_blocks.restype = _int
+    lib.fp8_block_gemm_quantize_blocks.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
     lib.fp8_block_gemm_version.restype = _int
     lib.fp8_block_gemm_version.argtypes = []
     _lib = lib
@@ -179,3 +181,29 @@ def quantize_rows(x: torch.Tensor, A: torch.Tensor = None, a_s: torch.Tensor = N
     if st != SUCCESS:
         raise FP8BGError(st, "fp8_block_gemm_quantize_rows")
     return A, a_s
+
+
+def quantize_blocks(w: torch.Tensor, B: torch.Tensor = None, b_s: torch.Tensor = None,
+                    stream: torch.cuda.Stream = None):
+    """128x128 block quantisation of bf16 weights w [N,K] into E4M3 codes
+    B [N,K] (float8_e4m3fn) and fp32 scales b_s [ceil(N/128), K/128]:
+    b_s = max(amax, 1e-12)/448 per block, B = E4M3_RNE(clamp(w / b_s, +-448)).
+    See fp8_block_gemm_quantize_blocks in include/fp8bg.h."""
+    lib = load()
+    if w.dim() != 2 or w.dtype != torch.bfloat16 or not w.is_contiguous() or not w.is_cuda:
+        raise ValueError("w must be a contiguous 2-D bfloat16 CUDA tensor")
+    N, K = w.shape
+    NB, G = (N + 127) // 128, (K + 127) // 128
+    if B is None:
+        B = torch.empty((N, K), dtype=torch.float8_e4m3fn, device=w.device)
+    else:
+        _check(B, "B", FP8_DTYPES, (N, K), w.device)
+    if b_s is None:
+        b_s = torch.empty((NB, G), dtype=torch.float32, device=w.device)
+    else:
+        _check(b_s, "b_s", (torch.float32,), (NB, G), w.device)
+    s = stream if stream is not None else torch.cuda.current_stream(w.device)
+    st = lib.fp8_block_gemm_quantize_blocks(w.data_ptr(), N, K, B.data_ptr(), b_s.data_ptr(), s.cuda_stream)
+    if st != SUCCESS:
+        raise FP8BGError(st, "fp8_block_gemm_quantize_blocks")
+    return B, b_s

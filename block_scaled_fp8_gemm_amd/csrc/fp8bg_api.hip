@@ -204,3 +204,21 @@ extern "C" int fp8_block_gemm_quantize_rows(const void* x, int64_t M, int64_t K,
                                                  M * G, static_cast<hipStream_t>(stream_));
   return e == hipSuccess ? FBG_SUCCESS : FBG_ERROR_HIP;
 }
+
+extern "C" int fp8_block_gemm_quantize_blocks(const void* w, int64_t N, int64_t K, void* B, float* b_s,
+                                              void* stream_) {
+  if (N < 0 || K < 0) return FBG_ERROR_INVALID_VALUE;
+  if (K % 128 != 0) return FBG_ERROR_UNSUPPORTED;
+  if (N > INT32_MAX || K > INT32_MAX) return FBG_ERROR_UNSUPPORTED;
+  const int64_t G = K / 128, NB = (N + 127) / 128;
+  const int64_t bytesW = N * K * 2, bytesB = N * K, bytesBs = NB * G * 4;
+  if ((bytesW > 0 && !w) || (bytesB > 0 && !B) || (bytesBs > 0 && !b_s)) return FBG_ERROR_INVALID_VALUE;
+  if (overlaps(B, bytesB, w, bytesW) || overlaps(b_s, bytesBs, w, bytesW) || overlaps(B, bytesB, b_s, bytesBs))
+    return FBG_ERROR_INVALID_VALUE;
+  if ((bytesW > 0 && !aligned(w, 16)) || (bytesB > 0 && !aligned(B, 8)) || (bytesBs > 0 && !aligned(b_s, 4)))
+    return FBG_ERROR_UNSUPPORTED;
+  if (N == 0 || K == 0) return FBG_SUCCESS;
+  const hipError_t e = fbg::launch_quantize_blocks(static_cast<const uint16_t*>(w), static_cast<uint8_t*>(B), b_s,
+                                                   (int)N, (int)K, static_cast<hipStream_t>(stream_));
+  return e == hipSuccess ? FBG_SUCCESS : FBG_ERROR_HIP;
+}

@@ -39,6 +39,7 @@ hipError_t launch_swap(const GemmArgs& a, int cfg, int64_t grid, int S, float* w
 hipError_t launch_short_k256(const GemmArgs& a, int cfg, int64_t grid);
 hipError_t launch_fill_zero(void* C, int64_t count, int out, hipStream_t stream);
 hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* q, float* a_s, int64_t groups, hipStream_t stream);
+hipError_t launch_quantize_blocks(const uint16_t* w, uint8_t* q, float* b_s, int N, int K, hipStream_t stream);
 #endif
 
 }  // namespace fbg

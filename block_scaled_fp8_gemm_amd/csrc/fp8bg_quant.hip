@@ -1,6 +1,7 @@
-// gfx950 kernel of the per-token 1x128 activation quantiser, the producer of
-// the GEMM's A and a_s:  bf16 x [M,K]  ->  OCP E4M3 codes A [M,K] and fp32
-// scales a_s [M, K/128].  (FlagGems-vllm PR #693, "feat: optimize w8a8 block
+// gfx950 kernels of the operand quantisers.  First the per-token 1x128
+// activation quantiser, the producer of the GEMM's A and a_s:  bf16 x [M,K]
+// ->  OCP E4M3 codes A [M,K] and fp32 scales a_s [M, K/128]; then the
+// 128x128 weight-block quantiser (below), the producer of B and b_s.  (FlagGems-vllm PR #693, "feat: optimize w8a8 block
 // fp8 matmul for Hopper", section "Description": per-token FP8 E4M3
 // activations with de-quant scales.)
 //
@@ -88,7 +89,77 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight quantisation, the producer of B and b_s: w [N,K] bf16 -> E4M3 codes
+// B [N,K] and one fp32 scale per 128 x 128 block, b_s [ceil(N/128), K/128]
+// (section "Description": [block_n, block_k] = [128, 128] weight scales).
+//
+//   b_s[nb,g] = max(max over the block of |w|, 1e-12) / 448
+//   B[n,k]    = E4M3 round-to-nearest-even of clamp(w[n,k] / b_s, -448, 448)
+//
+// One 256-thread workgroup per block: 16 lanes cover one 256-byte block row,
+// so the workgroup reads 16 rows per pass and 8 passes cover the block, all
+// 8 loads per lane in flight at once (rows past N read as zero and are not
+// stored).  The block maximum is a wave butterfly, then 4 values through LDS;
+// the quotient is formed as in the row quantiser (per-block reciprocal and
+// one correction step, the same E4M3 codes as the IEEE division).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quantize_blocks(const uint16_t* __restrict__ w, uint8_t* __restrict__ q,
+                                                         float* __restrict__ b_s, int N, int K) {
+  constexpr int kPasses = 8;
+  __shared__ float s_max[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = K / 128;
+  const int nb = blockIdx.x / G, g = blockIdx.x - nb * G;
+  const int row_in = tid >> 4, col = 128 * g + 8 * (tid & 15);
+  uint4 raw[kPasses];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int n = 128 * nb + 16 * p + row_in;
+    raw[p] = n < N ? *reinterpret_cast<const uint4*>(w + (int64_t)n * K + col) : make_uint4(0, 0, 0, 0);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const uint32_t v4[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v4[i])), fabsf(bf16_hi(v4[i]))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (lane == 0) s_max[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const float s = fmaxf(amax, 1e-12f) / 448.0f;
+  const float y = 1.0f / s;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int n = 128 * nb + 16 * p + row_in;
+    const uint32_t v4[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = (i & 1) ? bf16_hi(v4[i >> 1]) : bf16_lo(v4[i >> 1]);
+      const float t = v * y;
+      const float e = __builtin_fmaf(-t, s, v);
+      r[i] = clamp448(__builtin_copysignf(__builtin_fmaf(e, y, t), v));
+    }
+    if (n < N)
+      *reinterpret_cast<uint2*>(q + (int64_t)n * K + col) =
+          make_uint2(e4m3x4(r[0], r[1], r[2], r[3]), e4m3x4(r[4], r[5], r[6], r[7]));
+  }
+  if (tid == 0) b_s[blockIdx.x] = s;
+}
+
 }  // namespace
+
+hipError_t launch_quantize_blocks(const uint16_t* w, uint8_t* q, float* b_s, int N, int K, hipStream_t stream) {
+  const int64_t blocks = (int64_t)((N + 127) / 128) * (K / 128);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_quantize_blocks, dim3((unsigned)blocks), dim3(256), 0, stream, w, q, b_s, N, K);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* q, float* a_s, int64_t groups, hipStream_t stream) {
   const int64_t waves = (groups + 4 * kQuads - 1) / (4 * kQuads);

@@ -151,6 +151,25 @@ int fp8_block_gemm_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_c
  */
 int fp8_block_gemm_quantize_rows(const void *x, int64_t M, int64_t K, void *A, float *a_s, void *stream);
 
+/*
+ * fp8_block_gemm_quantize_blocks -- the producer of B and b_s: 128x128
+ * block quantisation of bf16 weights to OCP E4M3 (the section "Description"
+ * gives the GEMM FP8 E4M3 weights with [block_n, block_k] = [128, 128]
+ * de-quant scales; the scale maps each block's largest magnitude onto 448).
+ * For every block (nb, g) -- rows 128nb .. min(128nb+128, N), columns
+ * 128g .. 128g+128:
+ *
+ *     b_s[nb,g] = max(max over the block of |w[n,k]|, 1e-12f) / 448     (fp32 division)
+ *     B[n,k]    = E4M3 round-to-nearest-even of clamp(w[n,k] / b_s[nb,g], -448, 448)
+ *
+ * with w[n,k] / b_s an IEEE fp32 (correctly rounded) division.
+ * w: [N,K] bf16, row-major, 16-byte aligned (read); B: [N,K] E4M3 bytes,
+ * 8-byte aligned, and b_s: [ceil(N/128), K/128] fp32, 4-byte aligned
+ * (written in full).  Ownership, statuses and asynchrony as for
+ * fp8_block_gemm_quantize_rows; N may be any size >= 0.
+ */
+int fp8_block_gemm_quantize_blocks(const void *w, int64_t N, int64_t K, void *B, float *b_s, void *stream);
+
 /* fp8_block_gemm_status_string -- static text for a status code. */
 const char *fp8_block_gemm_status_string(int status);
 

@@ -193,3 +193,22 @@ def test_quantize_wrapper_checks():
         fbg.quantize_rows(torch.zeros(4, 128, dtype=torch.float32))
     with pytest.raises(ValueError):
         fbg.quantize_rows(torch.zeros(4, 128, dtype=torch.bfloat16))      # not on a GPU
+
+
+def _bcall(w=0x100000, N=300, K=256, B=0x200000, b_s=0x300000):
+    return fbg.load().fp8_block_gemm_quantize_blocks(w, N, K, B, b_s, None)
+
+
+def test_quantize_blocks_host_validation_statuses():
+    assert _bcall(w=None) == fbg.INVALID_VALUE
+    assert _bcall(B=None) == fbg.INVALID_VALUE
+    assert _bcall(b_s=None) == fbg.INVALID_VALUE
+    assert _bcall(N=-1) == fbg.INVALID_VALUE
+    assert _bcall(K=130) == fbg.UNSUPPORTED
+    assert _bcall(w=0x100004) == fbg.UNSUPPORTED
+    assert _bcall(B=0x200002) == fbg.UNSUPPORTED
+    assert _bcall(b_s=0x300001) == fbg.UNSUPPORTED
+    assert _bcall(B=0x100000 + 4096) == fbg.INVALID_VALUE     # B overlaps w (300*256*2 bytes)
+    assert _bcall(N=0, w=None, B=None, b_s=None) == fbg.SUCCESS
+    with pytest.raises(ValueError):
+        fbg.quantize_blocks(torch.zeros(4, 128, dtype=torch.bfloat16))

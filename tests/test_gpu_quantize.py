@@ -1,11 +1,12 @@
-"""GPU parity of the activation quantiser (fp8_block_gemm_quantize_rows,
-through the C ABI) with the CPU oracle: E4M3 codes and fp32 scales bit for
-bit.  Floating point decides an integer code here, so both sides take the
-decision from the same IEEE fp32 quotient x / a_s.
+"""GPU parity of the operand quantisers (fp8_block_gemm_quantize_rows and
+fp8_block_gemm_quantize_blocks, through the C ABI) with the CPU oracle: E4M3
+codes and fp32 scales bit for bit.  Floating point decides an integer code
+here, so both sides take the decision from the same IEEE fp32 quotient.
 
 Recipe: FlagGems-vllm PR #693, "feat: optimize w8a8 block fp8 matmul for
-Hopper", section "Description" (per-token FP8 E4M3 activations with
-de-quant scales); a_s = max(amax, 1e-12)/448 per 128-wide group.
+Hopper", section "Description" (per-token FP8 E4M3 activations and FP8 E4M3
+weights with [128, 128] block de-quant scales); scale = max(amax, 1e-12)/448
+per 1x128 activation group or 128x128 weight block.
 """
 import numpy as np
 import pytest
@@ -130,5 +131,50 @@ def test_quantised_activations_feed_the_gemm(gpu):
     sr_t = torch.from_numpy(sr).to("cuda:0")
     C1 = fbg.gemm(A, a_s, B, b_s)
     C2 = fbg.gemm(Ar, sr_t, B, b_s)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# 128 x 128 weight blocks (fp8_block_gemm_quantize_blocks).
+# ---------------------------------------------------------------------------
+def run_qb(bits: np.ndarray):
+    w = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    B, b_s = fbg.quantize_blocks(w)
+    torch.cuda.synchronize()
+    return B.view(torch.uint8).cpu().numpy(), b_s.cpu().numpy()
+
+
+@pytest.mark.parametrize("N,K", [(128, 128), (300, 256), (1, 384), (4096, 4096), (8192, 1024), (515, 640)])
+def test_weight_blocks_bitwise(gpu, N, K):
+    rng = np.random.default_rng(N + 7 * K)
+    w = (rng.normal(size=(N, K)) * 0.02).astype(np.float32)
+    if N > 200:
+        w[130:140, :] *= 300.0                     # a hot block row
+        w[N - 1, K - 1] = -7.0                     # the ragged last block's maximum
+        w[:128, 128:256 % K + 128 if K > 128 else 128] = 0.0
+    bits = bf16_bits(w)
+    q, s = run_qb(bits)
+    qr, sr = oracle.quantize_blocks(bits)
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32)), f"{N}x{K}: scales differ"
+    bad = np.argwhere(q != qr)
+    assert bad.size == 0, f"{N}x{K}: {len(bad)} codes differ, first at {bad[0].tolist()}"
+
+
+def test_quantised_weights_feed_the_gemm(gpu):
+    """End to end: both operands quantised on the GPU give the same GEMM bits
+    as the oracle-quantised ones."""
+    M, N, K = 64, 520, 1024
+    rng = np.random.default_rng(21)
+    xb = bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+    wb = bf16_bits((rng.normal(size=(N, K)) * 0.02).astype(np.float32))
+    dev = "cuda:0"
+    A, a_s = fbg.quantize_rows(torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16))
+    B, b_s = fbg.quantize_blocks(torch.from_numpy(wb.view(np.int16)).to(dev).view(torch.bfloat16))
+    qa, sa = oracle.quantize_rows(xb)
+    qb, sb = oracle.quantize_blocks(wb)
+    C1 = fbg.gemm(A, a_s, B, b_s)
+    C2 = fbg.gemm(torch.from_numpy(qa).to(dev).view(torch.float8_e4m3fn), torch.from_numpy(sa).to(dev),
+                  torch.from_numpy(qb).to(dev).view(torch.float8_e4m3fn), torch.from_numpy(sb).to(dev))
     torch.cuda.synchronize()
     assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
