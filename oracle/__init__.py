@@ -104,6 +104,32 @@ def block_gemm(A, a_s, B, b_s) -> np.ndarray:
     return C
 
 
+def grouped_gemm(A, a_s, B, b_s, offsets) -> np.ndarray:
+    """fp64 C[M,N] of the grouped (mixture-of-experts) block-scaled GEMM: the
+    rows offsets[e] .. offsets[e+1]-1 of A are the tokens routed to expert e
+    and are multiplied by that expert's weight B[e] with its block scales
+    b_s[e] -- the block-scaled GEMM of this module, once per expert (the
+    MoE-style traffic the first page's "Description" names; the expert
+    weights and per-expert token groups of the MoE kernel page).
+
+    A: uint8 [M,K]; a_s: float32 [M,G]; B: uint8 [E,N,K]; b_s: float32
+    [E, ceil(N/128), G]; offsets: E+1 non-decreasing integers from 0 to M.
+    """
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    b_s = np.ascontiguousarray(b_s, dtype=np.float32)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E, N, K = B.shape
+    M = A.shape[0]
+    if offsets.shape != (E + 1,) or offsets[0] != 0 or offsets[-1] != M or np.any(np.diff(offsets) < 0):
+        raise ValueError("offsets must be E+1 non-decreasing integers from 0 to M")
+    C = np.zeros((M, N), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            C[r0:r1] = block_gemm(A[r0:r1], a_s[r0:r1], B[e], b_s[e])
+    return C
+
+
 def round_bits(x, out_dtype) -> np.ndarray:
     """One-step RNE of fp64 values to out_dtype; returns the bit patterns
     (uint16 for bf16/fp16, uint32 for fp32) with x's shape."""
