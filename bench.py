@@ -23,6 +23,8 @@ Other modes (for profiles):
   --op quantize       time the per-token 1x128 activation quantiser (bf16 -> E4M3
                       codes + fp32 scales) on the workload's A shape instead
   --op quantize_weights   the 128x128 weight-block quantiser on the workload's B shape
+  --op grouped        the grouped (mixture-of-experts) GEMM on --moe NAME (default:
+                      64 tokens routed top-8 over 256 experts of 512 x 4096)
   --no-graph          launch each step eagerly (for counter collection)
 """
 import argparse
@@ -230,6 +232,73 @@ def run_quantize(args, w, M, torch, fbg, steps, warmup, use_graph=True, weights=
             "rows": M}
 
 
+def grouped_alg_bytes(d, out_bytes):
+    """A, a_s, the weights and scales of the experts that hold rows (the
+    others are never read), the offsets and C, each once."""
+    counts = d["offsets"][1:] - d["offsets"][:-1]
+    active = int((counts > 0).sum())
+    E, N, K = d["B"].shape
+    M, G = d["A"].shape[0], K // 128
+    return M * K + 4 * M * G + active * (N * K + 4 * ((N + 127) // 128) * G) + 4 * (E + 1) + M * N * out_bytes
+
+
+def run_grouped(args, mw, torch, fbg, W, steps, warmup, use_graph=True, out_name="bf16"):
+    """Times fp8_block_gemm_grouped on the MoE workload `mw`, rotating over
+    input copies (at least two: the weights alone exceed the MALL)."""
+    import numpy as np
+    out_dtype = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[out_name]
+    out_bytes = 4 if out_name == "fp32" else 2
+    d = W.make_moe_workload(mw)
+    dev = torch.device("cuda:0")
+    base = {
+        "A": torch.from_numpy(d["A"]).to(dev).view(torch.float8_e4m3fn),
+        "a_s": torch.from_numpy(d["a_s"]).to(dev),
+        "B": torch.from_numpy(d["B"]).to(dev).view(torch.float8_e4m3fn),
+        "b_s": torch.from_numpy(d["b_s"]).to(dev),
+        "offsets": torch.from_numpy(d["offsets"].astype(np.int32)).to(dev),
+    }
+    per_copy = sum(t.numel() * t.element_size() for t in base.values())
+    copies = max(2, min(args.max_copies, -(-2 * MALL_BYTES // per_copy)))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+    M, N = d["A"].shape[0], d["B"].shape[1]
+    outs = [torch.empty((M, N), dtype=out_dtype, device=dev) for _ in range(copies)]
+    stream = torch.cuda.Stream()
+    if args.cfg is not None:
+        os.environ["FBG_FORCE_CONFIG"] = str(args.cfg)
+
+    def step(i):
+        s = sets[i % copies]
+        fbg.grouped_gemm(s["A"], s["a_s"], s["B"], s["b_s"], s["offsets"], out_dtype=out_dtype,
+                         out=outs[i % copies], stream=stream)
+
+    gpu_ms, wall = time_steps(step, copies, steps, warmup, use_graph, stream, torch)
+    os.environ.pop("FBG_FORCE_CONFIG", None)
+    ms = gpu_ms / steps
+    nbytes = grouped_alg_bytes(d, out_bytes)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    flops = 2 * M * N * d["A"].shape[1]
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return {"d": d, "ms_per_step": ms, "gbs": gbs, "tflops": flops / (ms * 1e-3) / 1e12, "roof": roof,
+            "copies": copies, "alg_bytes": nbytes, "M": M, "N": N, "flops": flops}
+
+
+def cpu_baseline_grouped(d, flops_per_call, budget_s=12.0):
+    """The oracle's grouped GEMM over the full MoE workload, repeated until
+    about `budget_s` have passed."""
+    import oracle
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.grouped_gemm(d["A"], d["a_s"], d["B"], d["b_s"], d["offsets"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    return {"value": round(reps * flops_per_call / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"full MoE workload (fp64 oracle, every expert's GEMM) repeated {reps}x in {el:.1f} s"}
+
+
 def cpu_baseline_quantize(bits, budget_s=12.0, weights=False):
     """The oracle's row (or weight-block) quantiser, on the host's cores, over
     the full input repeated until about `budget_s` have passed."""
@@ -291,9 +360,10 @@ def main():
     ap.add_argument("--variant", default="auto", help="force a kernel variant (tuning)")
     ap.add_argument("--split", type=int, default=0, help="force a split-K count (tuning)")
     ap.add_argument("--cfg", type=int, default=None, help="force a tile configuration (tuning)")
-    ap.add_argument("--op", default="gemm", choices=["gemm", "quantize", "quantize_weights"],
+    ap.add_argument("--op", default="gemm", choices=["gemm", "quantize", "quantize_weights", "grouped"],
                     help="gemm (default), the activation quantiser on the workload's A shape, "
-                         "or the 128x128 weight quantiser on its B shape")
+                         "the 128x128 weight quantiser on its B shape, or the grouped MoE GEMM")
+    ap.add_argument("--moe", default="moe_decode_t64_e256_512x4096", help="MoE workload of --op grouped")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -337,6 +407,26 @@ def main():
                 print(json.dumps(line), flush=True)
         return
 
+    if args.op == "grouped":
+        mw = W.MOE_WORKLOADS[args.moe]
+        out = args.out or "bf16"
+        r = run_grouped(args, mw, torch, fbg, W, args.steps, args.warmup, not args.no_graph, out)
+        line = {
+            "metric": "HBM GB/s and % of roofline of the grouped (MoE) block-scaled FP8 GEMM, 1\u00d7MI355X",
+            "value": round(r["gbs"], 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 6), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+            "config": {"workload": mw.name, "tokens": mw.tokens, "experts": mw.experts, "top_k": mw.top_k,
+                       "rows": r["M"], "N": mw.N, "K": mw.K, "out_dtype": out,
+                       "active_experts": int((r["d"]["offsets"][1:] > r["d"]["offsets"][:-1]).sum()),
+                       "tflops": round(r["tflops"], 3), "input_copies": r["copies"],
+                       "graphs": not args.no_graph},
+            "roofline": dict(r["roof"], traffic=None),
+        }
+        if not args.no_cpu:
+            line["cpu_baseline"] = cpu_baseline_grouped(r["d"], r["flops"])
+        print(json.dumps(line), flush=True)
+        return
     w = W.WORKLOADS[args.workload]
     M = args.M if args.M is not None else w.M
     if args.op in ("quantize", "quantize_weights"):

@@ -65,6 +65,8 @@ def load():
     lib.fp8_block_gemm_quantize_rows.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
     lib.fp8_block_gemm_quantize_blocks.restype = _int
     lib.fp8_block_gemm_quantize_blocks.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
+    lib.fp8_block_gemm_grouped.restype = _int
+    lib.fp8_block_gemm_grouped.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]
     lib.fp8_block_gemm_version.restype = _int
     lib.fp8_block_gemm_version.argtypes = []
     _lib = lib
@@ -207,3 +209,35 @@ def quantize_blocks(w: torch.Tensor, B: torch.Tensor = None, b_s: torch.Tensor =
     if st != SUCCESS:
         raise FP8BGError(st, "fp8_block_gemm_quantize_blocks")
     return B, b_s
+
+
+def grouped_gemm(A: torch.Tensor, a_s: torch.Tensor, B: torch.Tensor, b_s: torch.Tensor, offsets: torch.Tensor,
+                 out_dtype=torch.bfloat16, out: torch.Tensor = None, stream: torch.cuda.Stream = None) -> torch.Tensor:
+    """Grouped (mixture-of-experts) block-scaled GEMM: rows offsets[e] ..
+    offsets[e+1]-1 of A use expert e's weight B[e] [N,K] and scales b_s[e].
+
+    A [M,K] E4M3, a_s [M,K/128] fp32, B [E,N,K] E4M3, b_s [E,ceil(N/128),K/128]
+    fp32, offsets int32 [E+1] on the same GPU.  See fp8_block_gemm_grouped in
+    include/fp8bg.h."""
+    lib = load()
+    if A.dim() != 2 or B.dim() != 3:
+        raise ValueError("A must be 2-D and B 3-D [E, N, K]")
+    M, K = A.shape
+    E, N = B.shape[0], B.shape[1]
+    G, NB = (K + 127) // 128, (N + 127) // 128
+    dev = A.device
+    _check(A, "A", FP8_DTYPES, (M, K), dev)
+    _check(B, "B", FP8_DTYPES, (E, N, K), dev)
+    _check(a_s, "a_s", (torch.float32,), (M, G), dev)
+    _check(b_s, "b_s", (torch.float32,), (E, NB, G), dev)
+    _check(offsets, "offsets", (torch.int32,), (E + 1,), dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    else:
+        _check(out, "out", (out_dtype,), (M, N), dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = lib.fp8_block_gemm_grouped(A.data_ptr(), a_s.data_ptr(), B.data_ptr(), b_s.data_ptr(), out.data_ptr(),
+                                    offsets.data_ptr(), E, M, N, K, _out_code(out_dtype), s.cuda_stream)
+    if st != SUCCESS:
+        raise FP8BGError(st, "fp8_block_gemm_grouped")
+    return out

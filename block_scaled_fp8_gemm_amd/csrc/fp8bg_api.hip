@@ -222,3 +222,52 @@ extern "C" int fp8_block_gemm_quantize_blocks(const void* w, int64_t N, int64_t 
                                                    (int)N, (int)K, static_cast<hipStream_t>(stream_));
   return e == hipSuccess ? FBG_SUCCESS : FBG_ERROR_HIP;
 }
+
+extern "C" int fp8_block_gemm_grouped(const void* A, const float* a_s, const void* B, const float* b_s, void* C,
+                                      const int32_t* offsets, int64_t E, int64_t M, int64_t N, int64_t K,
+                                      int out_dtype, void* stream_) {
+  if (E < 0 || M < 0 || N < 0 || K < 0) return FBG_ERROR_INVALID_VALUE;
+  if (out_dtype != FBG_OUT_BF16 && out_dtype != FBG_OUT_FP16 && out_dtype != FBG_OUT_FP32)
+    return FBG_ERROR_INVALID_VALUE;
+  if (K % 128 != 0) return FBG_ERROR_UNSUPPORTED;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || E > INT32_MAX - 1) return FBG_ERROR_UNSUPPORTED;
+  const int64_t G = K / 128, NB = (N + 127) / 128;
+  const int64_t bytesA = M * K, bytesAs = M * G * 4, bytesB = E * N * K, bytesBs = E * NB * G * 4;
+  const int64_t bytesC = M * N * elem_size(out_dtype), bytesOff = (E + 1) * 4;
+  if ((bytesA > 0 && !A) || (bytesAs > 0 && !a_s) || (bytesB > 0 && !B) || (bytesBs > 0 && !b_s) ||
+      (bytesC > 0 && !C) || (E > 0 && !offsets))
+    return FBG_ERROR_INVALID_VALUE;
+  if (overlaps(C, bytesC, A, bytesA) || overlaps(C, bytesC, B, bytesB) || overlaps(C, bytesC, a_s, bytesAs) ||
+      overlaps(C, bytesC, b_s, bytesBs) || overlaps(C, bytesC, offsets, bytesOff))
+    return FBG_ERROR_INVALID_VALUE;
+  if ((bytesA > 0 && !aligned(A, 16)) || (bytesB > 0 && !aligned(B, 16)) || (bytesAs > 0 && !aligned(a_s, 4)) ||
+      (bytesBs > 0 && !aligned(b_s, 4)) || (bytesC > 0 && !aligned(C, (uintptr_t)elem_size(out_dtype))) ||
+      (E > 0 && !aligned(offsets, 4)))
+    return FBG_ERROR_UNSUPPORTED;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (M == 0 || N == 0) return FBG_SUCCESS;
+  if (K == 0 || E == 0)  // the empty sum (no groups, or no expert to hold a row)
+    return fbg::launch_fill_zero(C, M * N, out_dtype, stream) == hipSuccess ? FBG_SUCCESS : FBG_ERROR_HIP;
+  const int cfg = fbg::grouped_cfg_for(M, E, N, K, forced_config());
+  if (cfg < 0) return FBG_ERROR_UNSUPPORTED;
+  const int64_t grid = fbg::grouped_grid(cfg, E, N);
+  if (grid > INT32_MAX) return FBG_ERROR_UNSUPPORTED;
+
+  fbg::GemmArgs args;
+  args.A = static_cast<const uint8_t*>(A);
+  args.a_s = a_s;
+  args.B = static_cast<const uint8_t*>(B);
+  args.b_s = b_s;
+  args.C = C;
+  args.M = (int)M;
+  args.N = (int)N;
+  args.K = (int)K;
+  args.out = out_dtype;
+  args.vec = (N % 4 == 0) && aligned(C, (uintptr_t)(4 * elem_size(out_dtype)));
+  args.stream = stream;
+  if (env_flag("FBG_LOG"))
+    fprintf(stderr, "fp8bg grouped: E=%lld M=%lld N=%lld K=%lld out=%d -> cfg=%d grid=%lld\n", (long long)E,
+            (long long)M, (long long)N, (long long)K, out_dtype, cfg, (long long)grid);
+  const hipError_t e = fbg::launch_grouped(args, cfg, grid, offsets, (int)E);
+  return e == hipSuccess ? FBG_SUCCESS : FBG_ERROR_HIP;
+}

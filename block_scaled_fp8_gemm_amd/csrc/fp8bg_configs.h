@@ -61,6 +61,15 @@ namespace fbg {
   X(14, 1, 2, 2, 1)       \
   X(15, 2, 2, 2, 1)
 
+// Grouped (mixture-of-experts) kernel: same fields as the skinny kernels.
+#define FBG_GROUPED_CFGS(X) \
+  X(0, 2, 1, 4, 1)          \
+  X(1, 2, 2, 4, 1)          \
+  X(2, 2, 4, 2, 1)          \
+  X(3, 1, 1, 4, 1)          \
+  X(4, 4, 1, 4, 1)          \
+  X(5, 2, 1, 8, 1)
+
 struct GenericCfg { int bm, bn, waves_m, waves_n, stages; };
 constexpr GenericCfg kGenericCfgs[] = {
 #define X(id, bm, bn, wm, wn, st) {bm, bn, wm, wn, st},
@@ -83,6 +92,13 @@ constexpr SkinnyCfg kShortCfgs[] = {
 #undef X
 };
 constexpr int kNumShortCfgs = sizeof(kShortCfgs) / sizeof(kShortCfgs[0]);
+
+constexpr SkinnyCfg kGroupedCfgs[] = {
+#define X(id, nb, mb, kw, gpw) {nb, mb, kw, gpw},
+    FBG_GROUPED_CFGS(X)
+#undef X
+};
+constexpr int kNumGroupedCfgs = sizeof(kGroupedCfgs) / sizeof(kGroupedCfgs[0]);
 
 inline int skinny_tile_n(const SkinnyCfg& c) { return 16 * c.nb16; }
 inline int skinny_tile_m(const SkinnyCfg& c) { return 16 * c.mb16; }

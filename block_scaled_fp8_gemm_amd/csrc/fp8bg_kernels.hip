@@ -242,6 +242,135 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 }
 
 // ===========================================================================
+// Building blocks of the skinny kernels.
+//
+// skinny_tile: this wave's FP32 partials of a workgroup tile of NB16 x MB16
+// 16x16 blocks (weight rows pb, activation rows pa with their a_s rows pas,
+// the tile's b_s block row pbs) over its chunks of the group range
+// [g_lo, g_hi).  Every wave loads its own B and A fragments straight from
+// global memory into registers, all loads of a chunk of GPW groups in flight
+// at once and the next chunk prefetched while the current one is computed.
+// The KW waves of a workgroup split the range: wave kw takes chunks kw,
+// kw+KW, ...
+//
+// skinny_reduce: sums the KW waves' partials through LDS in the fixed order
+// kw = 0..KW-1; wave w then owns blocks b with b % KW == w.
+// ===========================================================================
+template <int NB16, int MB16, int KW, int GPW, int KFIX>
+__device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint8_t* const* pa,
+                                            const float* const* pas, const float* pbs, int g_lo, int g_hi, int kw,
+                                            int lane, v4f (&acc)[NB16][MB16]) {
+  struct Chunk {
+    v8i bf[GPW][NB16];
+    v8i af[GPW][MB16];
+    float as[GPW][MB16];
+    float bs[GPW];
+  };
+  // Chunk c of this wave: groups g_lo + (c*KW + kw)*GPW + u, u < GPW.  Only
+  // chunks with at least one group in range are loaded; inside the last one,
+  // groups past the range are clamped (never computed).  Loads carry no
+  // per-group condition, so the compiler counts outstanding loads exactly
+  // and waits only for the chunk about to be used.
+  auto load = [&](Chunk& ch, int c) {
+    const int g0 = g_lo + (c * KW + kw) * GPW;
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      const int g = (g0 + u) < g_hi ? (g0 + u) : (g_hi - 1);
+      const int k0 = g * kGroup;
+#pragma unroll
+      for (int i = 0; i < NB16; ++i) ch.bf[u][i] = load_frag_global(pb[i] + k0, lane);
+#pragma unroll
+      for (int j = 0; j < MB16; ++j) ch.af[u][j] = load_frag_global(pa[j] + k0, lane);
+#pragma unroll
+      for (int j = 0; j < MB16; ++j) ch.as[u][j] = pas[j][g];
+      ch.bs[u] = pbs[g];
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < NB16; ++i)
+#pragma unroll
+    for (int j = 0; j < MB16; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Chunk& ch, int c) {
+    const int g0 = g_lo + (c * KW + kw) * GPW;
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      if (g0 + u < g_hi) {
+#pragma unroll
+        for (int j = 0; j < MB16; ++j) {
+          const float sc = ch.as[u][j] * ch.bs[u];  // a_s * b_s, once per group and lane
+#pragma unroll
+          for (int i = 0; i < NB16; ++i) {
+            const v4f p = mfma_group(ch.bf[u][i], ch.af[u][j]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], sc, acc[i][j][r]);
+          }
+        }
+      }
+    }
+  };
+
+  // Chunks of this wave that hold at least one group of [g_lo, g_hi).
+  const int first = g_lo + kw * GPW;
+  const int my_chunks = first < g_hi ? (g_hi - first + KW * GPW - 1) / (KW * GPW) : 0;
+  if constexpr (KFIX != 0) {
+    if (my_chunks > 0) {
+      Chunk ch;
+      load(ch, 0);
+      compute(ch, 0);
+    }
+  } else if (my_chunks > 0) {
+    // Two register buffers in ping-pong, no copies between them: chunk c+1
+    // is in flight while chunk c is computed.  The steady-state loop runs
+    // while two more chunks exist; the last one or two are peeled.
+    Chunk b0, b1;
+    load(b0, 0);
+    int c = 0;
+    for (; c + 2 < my_chunks; c += 2) {
+      load(b1, c + 1);
+      compute(b0, c);
+      load(b0, c + 2);
+      compute(b1, c + 1);
+    }
+    if (my_chunks - c == 2) {
+      load(b1, c + 1);
+      compute(b0, c);
+      compute(b1, c + 1);
+    } else {
+      compute(b0, c);
+    }
+  }
+
+}
+
+template <int NB16, int MB16, int KW, typename Red>
+__device__ __forceinline__ void skinny_reduce(Red& sRed, int kw, int lane, v4f (&acc)[NB16][MB16]) {
+  constexpr int NBLK = NB16 * MB16;
+  if constexpr (KW > 1) {
+#pragma unroll
+    for (int i = 0; i < NB16; ++i)
+#pragma unroll
+      for (int j = 0; j < MB16; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sRed[kw][i * MB16 + j][r][lane] = acc[i][j][r];
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      if (b % KW != kw) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = sRed[0][b][r][lane];
+#pragma unroll
+        for (int q = 1; q < KW; ++q) v += sRed[q][b][r][lane];
+        acc[b / MB16][b % MB16][r] = v;
+      }
+    }
+  }
+
+}
+
+// ===========================================================================
 // Skinny kernel: swap-AB, optionally split over K, and (KFIX = 2) the
 // short-K kernel.  (Section "Specialized kernels and the optimization idea":
 // swap_ab, swap_ab_splitk, short_k256.)
@@ -324,111 +453,11 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
   }
   const float* pbs = b_s + (int64_t)nb * G;
 
-  struct Chunk {
-    v8i bf[GPW][NB16];
-    v8i af[GPW][MB16];
-    float as[GPW][MB16];
-    float bs[GPW];
-  };
-  // Chunk c of this wave: groups g_lo + (c*KW + kw)*GPW + u, u < GPW.  Only
-  // chunks with at least one group in range are loaded; inside the last one,
-  // groups past the range are clamped (never computed).  Loads carry no
-  // per-group condition, so the compiler counts outstanding loads exactly
-  // and waits only for the chunk about to be used.
-  auto load = [&](Chunk& ch, int c) {
-    const int g0 = g_lo + (c * KW + kw) * GPW;
-#pragma unroll
-    for (int u = 0; u < GPW; ++u) {
-      const int g = (g0 + u) < g_hi ? (g0 + u) : (g_hi - 1);
-      const int k0 = g * kGroup;
-#pragma unroll
-      for (int i = 0; i < NB16; ++i) ch.bf[u][i] = load_frag_global(pb[i] + k0, lane);
-#pragma unroll
-      for (int j = 0; j < MB16; ++j) ch.af[u][j] = load_frag_global(pa[j] + k0, lane);
-#pragma unroll
-      for (int j = 0; j < MB16; ++j) ch.as[u][j] = pas[j][g];
-      ch.bs[u] = pbs[g];
-    }
-  };
-
   v4f acc[NB16][MB16];
-#pragma unroll
-  for (int i = 0; i < NB16; ++i)
-#pragma unroll
-    for (int j = 0; j < MB16; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](const Chunk& ch, int c) {
-    const int g0 = g_lo + (c * KW + kw) * GPW;
-#pragma unroll
-    for (int u = 0; u < GPW; ++u) {
-      if (g0 + u < g_hi) {
-#pragma unroll
-        for (int j = 0; j < MB16; ++j) {
-          const float sc = ch.as[u][j] * ch.bs[u];  // a_s * b_s, once per group and lane
-#pragma unroll
-          for (int i = 0; i < NB16; ++i) {
-            const v4f p = mfma_group(ch.bf[u][i], ch.af[u][j]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], sc, acc[i][j][r]);
-          }
-        }
-      }
-    }
-  };
-
-  // Chunks of this wave that hold at least one group of [g_lo, g_hi).
-  const int first = g_lo + kw * GPW;
-  const int my_chunks = first < g_hi ? (g_hi - first + KW * GPW - 1) / (KW * GPW) : 0;
-  if constexpr (KFIX != 0) {
-    if (my_chunks > 0) {
-      Chunk ch;
-      load(ch, 0);
-      compute(ch, 0);
-    }
-  } else if (my_chunks > 0) {
-    // Two register buffers in ping-pong, no copies between them: chunk c+1
-    // is in flight while chunk c is computed.  The steady-state loop runs
-    // while two more chunks exist; the last one or two are peeled.
-    Chunk b0, b1;
-    load(b0, 0);
-    int c = 0;
-    for (; c + 2 < my_chunks; c += 2) {
-      load(b1, c + 1);
-      compute(b0, c);
-      load(b0, c + 2);
-      compute(b1, c + 1);
-    }
-    if (my_chunks - c == 2) {
-      load(b1, c + 1);
-      compute(b0, c);
-      compute(b1, c + 1);
-    } else {
-      compute(b0, c);
-    }
-  }
-
-  // Sum the KW waves' partials in the fixed order kw = 0..KW-1; wave w then
-  // owns blocks b with b % KW == w for the rest of the epilogue.
-  if constexpr (KW > 1) {
-#pragma unroll
-    for (int i = 0; i < NB16; ++i)
-#pragma unroll
-      for (int j = 0; j < MB16; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sRed[kw][i * MB16 + j][r][lane] = acc[i][j][r];
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < NBLK; ++b) {
-      if (b % KW != kw) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = sRed[0][b][r][lane];
-#pragma unroll
-        for (int q = 1; q < KW; ++q) v += sRed[q][b][r][lane];
-        acc[b / MB16][b % MB16][r] = v;
-      }
-    }
-  }
+  skinny_tile<NB16, MB16, KW, GPW, KFIX>(pb, pa, pas, pbs, g_lo, g_hi, kw, lane, acc);
+  // The KW waves' partials, summed in the fixed order kw = 0..KW-1; wave w
+  // then owns blocks b with b % KW == w for the rest of the epilogue.
+  skinny_reduce<NB16, MB16, KW>(sRed, kw, lane, acc);
 
   if (S > 1) {
     // Publish this split's partial at device scope: agent-scope stores are
@@ -496,6 +525,82 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
     const int m = m0 + 16 * j + (lane & 15);
     const int cnt = N - n < 4 ? N - n : 4;
     if (m < M && cnt > 0) store4<OUT>(C, (int64_t)m * N + n, acc[i][j], cnt, vec_ok);
+  }
+}
+
+// ===========================================================================
+// Grouped (mixture-of-experts) kernel: rows offsets[e] .. offsets[e+1]-1 of A
+// are the tokens routed to expert e, multiplied by that expert's weight
+// B[e] ([N,K]) with its block scales b_s[e].  (MoE-style traffic: the first
+// page's section "Description"; per-expert token groups and the decode
+// swap-AB path: the MoE kernel page, section "Summary".)
+//
+// One workgroup per (expert, n-tile): it streams its weight rows once per
+// token tile and walks the expert's tokens in tiles of 16*MB16 (decode
+// experts hold a handful of tokens, so usually one tile), in the swap-AB
+// orientation and with the skinny kernels' K loop and fixed-order cross-wave
+// sum.  An expert with no tokens costs one offset read: its weights are
+// never touched.  The offsets stay on the device (no host synchronisation);
+// they are clamped into [0, M], so malformed offsets can only leave rows
+// unwritten, never address outside A or C.
+// ===========================================================================
+template <int NB16, int MB16, int KW, int GPW, int OUT>
+__global__ __launch_bounds__(64 * KW) void k_grouped(
+    const uint8_t* __restrict__ A, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
+    const float* __restrict__ b_s, void* __restrict__ C, const int* __restrict__ offsets, int E, int M, int N,
+    int K, int vec_ok) {
+  constexpr int BN = 16 * NB16, BMS = 16 * MB16, NBLK = NB16 * MB16;
+  static_assert(128 % BN == 0, "a tile's n rows must share one b_s block");
+  __shared__ __attribute__((aligned(16))) float sRed[KW > 1 ? KW : 1][NBLK][4][64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int kw = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = K / kGroup;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int lid = xcd_remap(blockIdx.x, E * tiles_n);
+  const int e = lid / tiles_n, tn = lid - e * tiles_n;
+  int lo = offsets[e], hi = offsets[e + 1];
+  lo = lo < 0 ? 0 : (lo > M ? M : lo);
+  hi = hi < lo ? lo : (hi > M ? M : hi);
+  if (lo >= hi) return;
+
+  const int n0 = tn * BN;
+  const int nblk = (N + 127) / 128;
+  const int nb = (n0 >> 7) < nblk ? (n0 >> 7) : nblk - 1;
+  const uint8_t* Be = B + (int64_t)e * N * K;
+  const float* pbs = b_s + ((int64_t)e * nblk + nb) * G;
+  const uint8_t* pb[NB16];
+#pragma unroll
+  for (int i = 0; i < NB16; ++i) {
+    const int r = n0 + 16 * i + (lane & 15);
+    pb[i] = Be + (int64_t)(r < N ? r : N - 1) * K;
+  }
+
+  for (int m0 = lo; m0 < hi; m0 += BMS) {
+    // Token rows past the expert's last are clamped to it (never stored).
+    const uint8_t* pa[MB16];
+    const float* pas[MB16];
+#pragma unroll
+    for (int j = 0; j < MB16; ++j) {
+      int r = m0 + 16 * j + (lane & 15);
+      r = r < hi ? r : hi - 1;
+      pa[j] = A + (int64_t)r * K;
+      pas[j] = a_s + (int64_t)r * G;
+    }
+    v4f acc[NB16][MB16];
+    skinny_tile<NB16, MB16, KW, GPW, 0>(pb, pa, pas, pbs, 0, G, kw, lane, acc);
+    skinny_reduce<NB16, MB16, KW>(sRed, kw, lane, acc);
+    // Block (i, j): lane holds n = 16i + 4*(lane>>4) + r, m = 16j + (lane & 15).
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      if (b % KW != kw) continue;
+      const int i = b / MB16, j = b % MB16;
+      const int n = n0 + 16 * i + 4 * (lane >> 4);
+      const int m = m0 + 16 * j + (lane & 15);
+      const int cnt = N - n < 4 ? N - n : 4;
+      if (m < hi && cnt > 0) store4<OUT>(C, (int64_t)m * N + n, acc[i][j], cnt, vec_ok);
+    }
+    if (m0 + BMS < hi) __syncthreads();  // the next token tile rewrites sRed
   }
 }
 
@@ -576,6 +681,35 @@ hipError_t launch_short_k256(const GemmArgs& a, int cfg, int64_t grid) {
 #define X(id, nb, mb, kw, gpw) \
   case id: return launch_skinny_t<nb, mb, kw, gpw, 2>(a, grid, 1, nullptr, nullptr);
     FBG_SHORT_CFGS(X)
+#undef X
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int NB16, int MB16, int KW, int GPW>
+static hipError_t launch_grouped_t(const GemmArgs& a, int64_t grid, const int* offsets, int E) {
+  const dim3 blk(64 * KW);
+  switch (a.out) {
+    case kOutBF16:
+      hipLaunchKernelGGL((k_grouped<NB16, MB16, KW, GPW, kOutBF16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
+                         a.b_s, a.C, offsets, E, a.M, a.N, a.K, a.vec);
+      break;
+    case kOutFP16:
+      hipLaunchKernelGGL((k_grouped<NB16, MB16, KW, GPW, kOutFP16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
+                         a.b_s, a.C, offsets, E, a.M, a.N, a.K, a.vec);
+      break;
+    default:
+      hipLaunchKernelGGL((k_grouped<NB16, MB16, KW, GPW, kOutFP32>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
+                         a.b_s, a.C, offsets, E, a.M, a.N, a.K, a.vec);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped(const GemmArgs& a, int cfg, int64_t grid, const int* offsets, int E) {
+  switch (cfg) {
+#define X(id, nb, mb, kw, gpw) \
+  case id: return launch_grouped_t<nb, mb, kw, gpw>(a, grid, offsets, E);
+    FBG_GROUPED_CFGS(X)
 #undef X
     default: return hipErrorInvalidValue;
   }

@@ -168,6 +168,25 @@ int64_t workspace_bytes(const fbg_plan& p, int64_t M, int64_t N) {
   return workspace_counter_offset(p, M, N) + T * 4;
 }
 
+// Grouped: by the mean number of tokens per expert -- 32 n x 16 m tiles
+// (config 0) for decode-sized groups, 32 n x 32 m (config 1) up to 32, and
+// 32 n x 64 m (config 2) above, so each expert's weight rows are streamed
+// once per few token tiles.  force_cfg >= 0 picks a configuration; -1 is
+// returned for one that does not exist.
+int grouped_cfg_for(int64_t M, int64_t E, int64_t N, int64_t K, int force_cfg) {
+  (void)N;
+  (void)K;
+  if (force_cfg >= 0) return force_cfg < kNumGroupedCfgs ? force_cfg : -1;
+  const int64_t per = E > 0 ? cdiv(M, E) : M;
+  if (per <= 16) return 0;
+  if (per <= 32) return 1;
+  return 2;
+}
+
+int64_t grouped_grid(int cfg, int64_t E, int64_t N) {
+  return E * cdiv(N, skinny_tile_n(kGroupedCfgs[cfg]));
+}
+
 }  // namespace fbg
 
 extern "C" int fp8_block_gemm_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int variant,

@@ -130,6 +130,32 @@ int fp8_block_gemm_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_c
                         int variant, int split_k, fbg_plan *out);
 
 /*
+ * fp8_block_gemm_grouped -- the grouped (mixture-of-experts) form: E experts
+ * with their own weights, the tokens grouped by expert (the first page's
+ * section "Description" names the MoE-style traffic these GEMMs serve; the
+ * MoE kernel page, section "Summary", its per-expert token groups and decode
+ * swap-AB path).  For every expert e and row m in [offsets[e], offsets[e+1]):
+ *
+ *     C[m,n] = sum_g a_s[m,g] * b_s[e, n/128, g] * sum_{k in group g} A[m,k] * B[e,n,k]
+ *
+ * A [M,K], a_s [M,K/128] and C [M,N] as for fp8_block_gemm; B [E,N,K] E4M3
+ * (expert e's weight at B + e*N*K), b_s [E, ceil(N/128), K/128] fp32.
+ * offsets: DEVICE pointer to E+1 int32, non-decreasing, offsets[0] = 0,
+ * offsets[E] = M (typically written by the router on the GPU, so the call
+ * never synchronises with the host).  The kernel clamps every offset into
+ * [0, M]: malformed offsets can leave rows of C unwritten but never make it
+ * read or write outside A, a_s or C.  Rows of C outside every expert's
+ * range are not written.  M, N, K, E >= 0 with K % 128 == 0; M == 0 or
+ * N == 0: nothing launched; K == 0 or E == 0: C is filled with zeros.
+ * Alignment as for fp8_block_gemm, offsets 4-byte aligned; statuses as for
+ * fp8_block_gemm (C overlapping any input -> INVALID_VALUE).  No workspace;
+ * asynchronous on `stream`; deterministic.
+ */
+int fp8_block_gemm_grouped(const void *A, const float *a_s, const void *B, const float *b_s, void *C,
+                           const int32_t *offsets, int64_t E, int64_t M, int64_t N, int64_t K,
+                           int out_dtype, void *stream);
+
+/*
  * fp8_block_gemm_quantize_rows -- the producer of A and a_s: per-token 1x128
  * quantisation of bf16 activations to OCP E4M3 (the section "Description"
  * gives the GEMM per-token FP8 E4M3 activations with one de-quant scale per

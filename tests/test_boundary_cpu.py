@@ -165,6 +165,8 @@ def test_every_tile_configuration_has_parity_cases():
     assert ids("FBG_GENERIC_CFGS") <= have["generic"]
     assert ids("FBG_SWAP_CFGS") <= have["swap_ab"]
     assert ids("FBG_SHORT_CFGS") <= have["short_k256"]
+    from tests.test_gpu_grouped import GROUPED_CASES
+    assert ids("FBG_GROUPED_CFGS") <= {c[0] for c in GROUPED_CASES}
 
 
 def _qcall(x=0x100000, M=4, K=256, A=0x200000, a_s=0x300000):
@@ -212,3 +214,45 @@ def test_quantize_blocks_host_validation_statuses():
     assert _bcall(N=0, w=None, B=None, b_s=None) == fbg.SUCCESS
     with pytest.raises(ValueError):
         fbg.quantize_blocks(torch.zeros(4, 128, dtype=torch.bfloat16))
+
+
+def _gcall(A=0x100000, a_s=0x200000, B=0x300000, b_s=0x400000, C=0x50000000, off=0x600000, E=4, M=16, N=256,
+           K=256, out=0):
+    return fbg.load().fp8_block_gemm_grouped(A, a_s, B, b_s, C, off, E, M, N, K, out, None)
+
+
+def test_grouped_host_validation_statuses():
+    # As above: every case fails validation (or is empty) before any HIP call.
+    assert _gcall(A=None) == fbg.INVALID_VALUE
+    assert _gcall(a_s=None) == fbg.INVALID_VALUE
+    assert _gcall(B=None) == fbg.INVALID_VALUE
+    assert _gcall(b_s=None) == fbg.INVALID_VALUE
+    assert _gcall(C=None) == fbg.INVALID_VALUE
+    assert _gcall(off=None) == fbg.INVALID_VALUE
+    assert _gcall(E=-1) == fbg.INVALID_VALUE
+    assert _gcall(M=-1) == fbg.INVALID_VALUE
+    assert _gcall(out=5) == fbg.INVALID_VALUE
+    assert _gcall(K=200) == fbg.UNSUPPORTED
+    assert _gcall(A=0x100008) == fbg.UNSUPPORTED            # A not 16-byte aligned
+    assert _gcall(B=0x300004) == fbg.UNSUPPORTED
+    assert _gcall(b_s=0x400002) == fbg.UNSUPPORTED
+    assert _gcall(off=0x600002) == fbg.UNSUPPORTED          # offsets not 4-byte aligned
+    assert _gcall(C=0x50000001) == fbg.UNSUPPORTED
+    assert _gcall(C=0x300000 + 4096) == fbg.INVALID_VALUE   # C overlaps B (4*256*256 bytes)
+    assert _gcall(C=0x600000 - 64) == fbg.INVALID_VALUE     # C overlaps the offsets
+    assert _gcall(M=0, A=None, a_s=None, C=None) == fbg.SUCCESS   # empty: nothing launched
+    assert _gcall(N=0, B=None, b_s=None, C=None) == fbg.SUCCESS
+
+
+def test_grouped_wrapper_checks():
+    A = torch.zeros((5, 256), dtype=torch.float8_e4m3fn)
+    B = torch.zeros((2, 130, 256), dtype=torch.float8_e4m3fn)
+    a_s, b_s = torch.zeros((5, 2)), torch.zeros((2, 2, 2))
+    with pytest.raises(ValueError):       # offsets need E + 1 entries
+        fbg.grouped_gemm(A, a_s, B, b_s, torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(TypeError):
+        fbg.grouped_gemm(A, a_s, B, b_s, torch.zeros(3, dtype=torch.int64))
+    with pytest.raises(ValueError):       # B must be [E, N, K]
+        fbg.grouped_gemm(A, a_s, B[0], b_s, torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        fbg.grouped_gemm(A, a_s, B, torch.zeros((2, 1, 2)), torch.zeros(3, dtype=torch.int32))

@@ -164,3 +164,89 @@ def make_exact_inputs(M: int, N: int, K: int, seed: int, int_range: int = 4,
         "b_s": np.ldexp(np.float32(1.0), v).astype(np.float32),
         "Ai": Ai, "Bi": Bi, "u": u, "v": v,
     }
+
+
+# ---------------------------------------------------------------------------
+# Grouped (mixture-of-experts) inputs: tokens routed top-k over E experts,
+# the routed rows grouped by expert, one weight [N,K] per expert.  Shapes of
+# the MoE kernel page (section "Performance": the Flash shape's 256 experts,
+# t16 .. t1024 tokens) with the first page's decode weight shape
+# (N=512, K=4096); routing is uniform, each token picks top_k distinct
+# experts.
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class MoEWorkload:
+    name: str
+    tokens: int
+    experts: int
+    top_k: int
+    N: int
+    K: int
+    seed: int
+    note: str = ""
+
+
+MOE_WORKLOADS = {
+    "moe_decode_t64_e256_512x4096": MoEWorkload("moe_decode_t64_e256_512x4096", 64, 256, 8, 512, 4096, seed=11,
+                                                note="MoE decode: 64 tokens, top-8 of 256 experts, expert weight 512x4096"),
+}
+
+
+def route_counts(tokens: int, experts: int, top_k: int, seed: int) -> np.ndarray:
+    """Rows per expert when each token picks top_k distinct experts uniformly."""
+    rng = np.random.default_rng(seed)
+    picks = np.argsort(rng.random((tokens, experts)), axis=1)[:, :top_k]
+    return np.bincount(picks.ravel(), minlength=experts).astype(np.int64)
+
+
+def offsets_of(counts) -> np.ndarray:
+    return np.concatenate([[0], np.cumsum(np.asarray(counts, dtype=np.int64))]).astype(np.int64)
+
+
+def make_grouped_inputs(counts, N: int, K: int, seed: int, chunk_experts: int = 16):
+    """Standard recipe per expert: dict(A [M,K], a_s [M,G], B [E,N,K],
+    b_s [E,ceil(N/128),G], offsets [E+1]) as numpy arrays.  The activations
+    of the routed rows follow the activation recipe, every expert's weight the
+    weight recipe (its own 128x128 blocks)."""
+    if K % GROUP:
+        raise ValueError("the recipe quantises whole 128-wide groups")
+    counts = np.asarray(counts, dtype=np.int64)
+    E = len(counts)
+    offsets = offsets_of(counts)
+    M = int(offsets[-1])
+    rng = np.random.default_rng(seed)
+    A, a_s = quantize_rows(rng.standard_normal((M, K), dtype=np.float32))
+    G, NB = groups(K), (N + GROUP - 1) // GROUP
+    B = np.empty((E, N, K), dtype=np.uint8)
+    b_s = np.empty((E, NB, G), dtype=np.float32)
+    for e0 in range(0, E, chunk_experts):
+        e1 = min(E, e0 + chunk_experts)
+        w = rng.standard_normal((e1 - e0, N, K), dtype=np.float32) * np.float32(0.02)
+        if N % GROUP == 0:      # blocks never straddle two experts: one call for the chunk
+            q, s = quantize_blocks(w.reshape(-1, K))
+            B[e0:e1] = q.reshape(e1 - e0, N, K)
+            b_s[e0:e1] = s.reshape(e1 - e0, NB, G)
+        else:
+            for e in range(e0, e1):
+                B[e], b_s[e] = quantize_blocks(w[e - e0])
+    return {"A": A, "a_s": a_s, "B": B, "b_s": b_s, "offsets": offsets}
+
+
+def make_moe_workload(w: MoEWorkload):
+    counts = route_counts(w.tokens, w.experts, w.top_k, w.seed)
+    return make_grouped_inputs(counts, w.N, w.K, w.seed + 1)
+
+
+def make_exact_grouped_inputs(counts, N: int, K: int, seed: int, int_range: int = 4):
+    """Integer-valued codes and power-of-two scales (as make_exact_inputs),
+    per expert: every partial sum is exact in fp32."""
+    counts = np.asarray(counts, dtype=np.int64)
+    E = len(counts)
+    offsets = offsets_of(counts)
+    M = int(offsets[-1])
+    d = make_exact_inputs(M, N * E, K, seed, int_range=int_range)
+    G, NB = groups(K), (N + GROUP - 1) // GROUP
+    rng = np.random.default_rng(seed + 1)
+    v = rng.integers(-2, 2, size=(E, NB, G))
+    return {"A": d["A"], "a_s": d["a_s"], "B": d["B"].reshape(E, N, K),
+            "b_s": np.ldexp(np.float32(1.0), v).astype(np.float32), "offsets": offsets}
