@@ -55,21 +55,29 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(workload, plan, out):
-    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE profile
-    of this workload, if that profile was taken on the same kernel sources and
-    the same plan; else None."""
+def traffic_record(workload):
+    """The machine-readable record of the committed FETCH_SIZE / WRITE_SIZE
+    profile of `workload`, or None."""
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     for line in open(path):
         if line.startswith("traffic_record:"):
-            rec = json.loads(line.split(":", 1)[1])
-            same = (rec.get("source_hash") == kernel_source_hash() and rec.get("variant") == plan["variant_name"]
-                    and rec.get("config") == plan["config"] and rec.get("split_k") == plan["split_k"]
-                    and rec.get("out") == out)
-            return rec["traffic_bytes"] if same else None
+            return json.loads(line.split(":", 1)[1])
     return None
+
+
+def profiled_traffic(workload, plan, out):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE profile
+    of this workload, if that profile was taken on the same kernel sources and
+    the same plan; else None."""
+    rec = traffic_record(workload)
+    if rec is None:
+        return None
+    same = (rec.get("source_hash") == kernel_source_hash() and rec.get("variant") == plan["variant_name"]
+            and rec.get("config") == plan["config"] and rec.get("split_k") == plan["split_k"]
+            and rec.get("out") == out)
+    return rec["traffic_bytes"] if same else None
 
 
 def alg_bytes(M, N, K, out_bytes):
@@ -279,8 +287,9 @@ def run_grouped(args, mw, torch, fbg, W, steps, warmup, use_graph=True, out_name
     flops = 2 * M * N * d["A"].shape[1]
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    cfg = args.cfg if args.cfg is not None else fbg.grouped_plan(mw.experts, M, N, d["A"].shape[1])["config"]
     return {"d": d, "ms_per_step": ms, "gbs": gbs, "tflops": flops / (ms * 1e-3) / 1e12, "roof": roof,
-            "copies": copies, "alg_bytes": nbytes, "M": M, "N": N, "flops": flops}
+            "copies": copies, "alg_bytes": nbytes, "M": M, "N": N, "flops": flops, "cfg": cfg}
 
 
 def cpu_baseline_grouped(d, flops_per_call, budget_s=12.0):
@@ -423,6 +432,11 @@ def main():
                        "graphs": not args.no_graph},
             "roofline": dict(r["roof"], traffic=None),
         }
+        rec = traffic_record(mw.name)
+        if (rec is not None and args.cfg is None and rec.get("source_hash") == kernel_source_hash()
+                and rec.get("variant") == "grouped" and rec.get("config") == r["cfg"] and rec.get("out") == out):
+            line["roofline"]["traffic"] = rec["traffic_bytes"]
+        line["config"]["cfg"] = r["cfg"]
         if not args.no_cpu:
             line["cpu_baseline"] = cpu_baseline_grouped(r["d"], r["flops"])
         print(json.dumps(line), flush=True)

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8bg.so")
 SUCCESS, INVALID_VALUE, UNSUPPORTED, OUT_OF_MEMORY, HIP_ERROR = 0, 1, 2, 3, 4
 VARIANTS = {"auto": 0, "generic": 1, "short_k256": 2, "swap_ab": 3, "swap_ab_splitk": 4}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
+VARIANT_NAMES[5] = "grouped"          # reported by grouped_plan only
 OUT_CODES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
 OUT_DTYPES = {v: k for k, v in OUT_CODES.items()}
 FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)
@@ -67,6 +68,8 @@ def load():
     lib.fp8_block_gemm_quantize_blocks.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
     lib.fp8_block_gemm_grouped.restype = _int
     lib.fp8_block_gemm_grouped.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]
+    lib.fp8_block_gemm_grouped_plan.restype = _int
+    lib.fp8_block_gemm_grouped_plan.argtypes = [_i64, _i64, _i64, _i64, _vp]
     lib.fp8_block_gemm_version.restype = _int
     lib.fp8_block_gemm_version.argtypes = []
     _lib = lib
@@ -95,6 +98,17 @@ def plan(M: int, N: int, K: int, out_dtype=torch.bfloat16, cu_count: int = 256,
                                     split_k, ctypes.byref(p))
     if st != SUCCESS:
         raise FP8BGError(st, "fp8_block_gemm_plan")
+    d = {f: getattr(p, f) for f, _ in Plan._fields_}
+    d["variant_name"] = VARIANT_NAMES.get(p.variant, "none")
+    return d
+
+
+def grouped_plan(E: int, M: int, N: int, K: int) -> dict:
+    """The grouped GEMM's tile choice for E experts holding M rows (pure host call)."""
+    p = Plan()
+    st = load().fp8_block_gemm_grouped_plan(E, M, N, K, ctypes.byref(p))
+    if st != SUCCESS:
+        raise FP8BGError(st, "fp8_block_gemm_grouped_plan")
     d = {f: getattr(p, f) for f, _ in Plan._fields_}
     d["variant_name"] = VARIANT_NAMES.get(p.variant, "none")
     return d

@@ -12,7 +12,10 @@ namespace fbg {
   X(0, 128, 128, 2, 2, 4)   \
   X(1, 256, 128, 2, 2, 3)   \
   X(2, 64, 128, 1, 2, 4)    \
-  X(3, 256, 256, 2, 4, 2)
+  X(3, 256, 256, 2, 4, 2)   \
+  X(4, 64, 64, 1, 2, 4)     \
+  X(5, 128, 64, 2, 2, 3)    \
+  X(6, 64, 32, 1, 2, 4)
 
 // Skinny kernels (swap-AB and its split-K form): id, NB16 16-row blocks of
 // weight rows (output columns n), MB16 16-column blocks of activation rows
@@ -68,7 +71,12 @@ namespace fbg {
   X(2, 2, 4, 2, 1)          \
   X(3, 1, 1, 4, 1)          \
   X(4, 4, 1, 4, 1)          \
-  X(5, 2, 1, 8, 1)
+  X(5, 2, 1, 8, 1)          \
+  X(6, 4, 4, 2, 1)          \
+  X(7, 4, 2, 4, 1)          \
+  X(8, 2, 4, 4, 1)          \
+  X(9, 4, 4, 4, 1)          \
+  X(10, 8, 2, 2, 1)
 
 struct GenericCfg { int bm, bn, waves_m, waves_n, stages; };
 constexpr GenericCfg kGenericCfgs[] = {

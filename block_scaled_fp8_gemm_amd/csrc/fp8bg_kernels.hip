@@ -536,14 +536,48 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
 // swap-AB path: the MoE kernel page, section "Summary".)
 //
 // One workgroup per (expert, n-tile): it streams its weight rows once per
-// token tile and walks the expert's tokens in tiles of 16*MB16 (decode
-// experts hold a handful of tokens, so usually one tile), in the swap-AB
-// orientation and with the skinny kernels' K loop and fixed-order cross-wave
-// sum.  An expert with no tokens costs one offset read: its weights are
-// never touched.  The offsets stay on the device (no host synchronisation);
-// they are clamped into [0, M], so malformed offsets can only leave rows
-// unwritten, never address outside A or C.
+// token tile and walks the expert's tokens in tiles of up to 16*MB16 rows
+// (decode experts hold a handful of tokens, so usually one tile), in the
+// swap-AB orientation and with the skinny kernels' K loop and fixed-order
+// cross-wave sum.  A tile computes only its 16-row blocks that hold tokens:
+// the count of such blocks selects one of MB16 straight-line instances, so a
+// 20-token expert loads and multiplies 2 blocks, not MB16.  An expert with no
+// tokens costs one offset read: its weights are never touched.  The offsets
+// stay on the device (no host synchronisation); they are clamped into
+// [0, M], so malformed offsets can only leave rows unwritten, never address
+// outside A or C.
 // ===========================================================================
+template <int NB16, int MBA, int KW, int GPW, int OUT, typename Red>
+__device__ __forceinline__ void grouped_mtile(const uint8_t* const* pb, const float* pbs, const uint8_t* A,
+                                              const float* a_s, void* C, Red& sRed, int m0, int hi, int n0, int N,
+                                              int K, int G, int kw, int lane, int vec_ok) {
+  // Token rows past the expert's last are clamped to it (never stored).
+  const uint8_t* pa[MBA];
+  const float* pas[MBA];
+#pragma unroll
+  for (int j = 0; j < MBA; ++j) {
+    int r = m0 + 16 * j + (lane & 15);
+    r = r < hi ? r : hi - 1;
+    pa[j] = A + (int64_t)r * K;
+    pas[j] = a_s + (int64_t)r * G;
+  }
+  v4f acc[NB16][MBA];
+  skinny_tile<NB16, MBA, KW, GPW, 0>(pb, pa, pas, pbs, 0, G, kw, lane, acc);
+  // The first NB16*MBA blocks of the reduction buffer, in this tile's shape.
+  auto& red = *reinterpret_cast<float(*)[KW > 1 ? KW : 1][NB16 * MBA][4][64]>(&sRed[0][0][0][0]);
+  skinny_reduce<NB16, MBA, KW>(red, kw, lane, acc);
+  // Block (i, j): lane holds n = 16i + 4*(lane>>4) + r, m = 16j + (lane & 15).
+#pragma unroll
+  for (int b = 0; b < NB16 * MBA; ++b) {
+    if (b % KW != kw) continue;
+    const int i = b / MBA, j = b % MBA;
+    const int n = n0 + 16 * i + 4 * (lane >> 4);
+    const int m = m0 + 16 * j + (lane & 15);
+    const int cnt = N - n < 4 ? N - n : 4;
+    if (m < hi && cnt > 0) store4<OUT>(C, (int64_t)m * N + n, acc[i][j], cnt, vec_ok);
+  }
+}
+
 template <int NB16, int MB16, int KW, int GPW, int OUT>
 __global__ __launch_bounds__(64 * KW) void k_grouped(
     const uint8_t* __restrict__ A, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
@@ -551,6 +585,7 @@ __global__ __launch_bounds__(64 * KW) void k_grouped(
     int K, int vec_ok) {
   constexpr int BN = 16 * NB16, BMS = 16 * MB16, NBLK = NB16 * MB16;
   static_assert(128 % BN == 0, "a tile's n rows must share one b_s block");
+  static_assert(MB16 >= 1 && MB16 <= 4, "up to 4 token blocks per tile");
   __shared__ __attribute__((aligned(16))) float sRed[KW > 1 ? KW : 1][NBLK][4][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -577,29 +612,19 @@ __global__ __launch_bounds__(64 * KW) void k_grouped(
   }
 
   for (int m0 = lo; m0 < hi; m0 += BMS) {
-    // Token rows past the expert's last are clamped to it (never stored).
-    const uint8_t* pa[MB16];
-    const float* pas[MB16];
-#pragma unroll
-    for (int j = 0; j < MB16; ++j) {
-      int r = m0 + 16 * j + (lane & 15);
-      r = r < hi ? r : hi - 1;
-      pa[j] = A + (int64_t)r * K;
-      pas[j] = a_s + (int64_t)r * G;
-    }
-    v4f acc[NB16][MB16];
-    skinny_tile<NB16, MB16, KW, GPW, 0>(pb, pa, pas, pbs, 0, G, kw, lane, acc);
-    skinny_reduce<NB16, MB16, KW>(sRed, kw, lane, acc);
-    // Block (i, j): lane holds n = 16i + 4*(lane>>4) + r, m = 16j + (lane & 15).
-#pragma unroll
-    for (int b = 0; b < NBLK; ++b) {
-      if (b % KW != kw) continue;
-      const int i = b / MB16, j = b % MB16;
-      const int n = n0 + 16 * i + 4 * (lane >> 4);
-      const int m = m0 + 16 * j + (lane & 15);
-      const int cnt = N - n < 4 ? N - n : 4;
-      if (m < hi && cnt > 0) store4<OUT>(C, (int64_t)m * N + n, acc[i][j], cnt, vec_ok);
-    }
+    const int rows = hi - m0 < BMS ? hi - m0 : BMS;
+    const int mba = __builtin_amdgcn_readfirstlane((rows + 15) >> 4);  // token blocks of this tile
+    if (MB16 >= 4 && mba >= 4)
+      grouped_mtile<NB16, (MB16 >= 4 ? 4 : 1), KW, GPW, OUT>(pb, pbs, A, a_s, C, sRed, m0, hi, n0, N, K, G, kw,
+                                                              lane, vec_ok);
+    else if (MB16 >= 3 && mba == 3)
+      grouped_mtile<NB16, (MB16 >= 3 ? 3 : 1), KW, GPW, OUT>(pb, pbs, A, a_s, C, sRed, m0, hi, n0, N, K, G, kw,
+                                                              lane, vec_ok);
+    else if (MB16 >= 2 && mba == 2)
+      grouped_mtile<NB16, (MB16 >= 2 ? 2 : 1), KW, GPW, OUT>(pb, pbs, A, a_s, C, sRed, m0, hi, n0, N, K, G, kw,
+                                                              lane, vec_ok);
+    else
+      grouped_mtile<NB16, 1, KW, GPW, OUT>(pb, pbs, A, a_s, C, sRed, m0, hi, n0, N, K, G, kw, lane, vec_ok);
     if (m0 + BMS < hi) __syncthreads();  // the next token tile rewrites sRed
   }
 }

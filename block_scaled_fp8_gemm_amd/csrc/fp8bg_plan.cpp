@@ -53,15 +53,51 @@ int short_cfg_for(int64_t M) {
   return 6;
 }
 
-// Generic: the largest tile that still gives every compute unit a
-// workgroup -- 256 x 256 (8 waves, the highest MFMA work per LDS byte),
-// then 256 x 128, then 128 x 128 -- else 64 x 128 (the most workgroups).
+// Generic: each compute unit pulls its tiles' A and B rows at a roughly
+// fixed rate (~25 GB/s per CU on this GPU, whatever the tile), so a launch
+// costs about (workgroups per CU) x (BM + BN) x K bytes per CU.  The planner
+// takes the configuration with the fewest such bytes; on a tie, the larger
+// tile (more MFMA work per LDS byte, fewer workgroups), then more waves.  For large M this is
+// the 256 x 256 tile; in the mid-M band it picks the small tiles that put a
+// workgroup on every CU (measured: M = 128, N = 8192, K = 1024 runs in
+// 6.8 us with 64 x 64 tiles against 9.3 us with 64 x 128).
+int64_t generic_cost(const GenericCfg& g, int64_t M, int64_t N, int cu) {
+  const int64_t wgs = cdiv(M, g.bm) * cdiv(N, g.bn);
+  return cdiv(wgs, cu) * (g.bm + g.bn);
+}
+
 int generic_cfg_for(int64_t M, int64_t N, int cu) {
-  if (M <= 64) return 2;
-  if (cdiv(M, 256) * cdiv(N, 256) >= (int64_t)cu) return 3;
-  if (cdiv(M, 256) * cdiv(N, 128) >= (int64_t)cu) return 1;
-  if (cdiv(M, 128) * cdiv(N, 128) >= (int64_t)cu) return 0;
-  return 2;
+  int best = 0;
+  for (int c = 1; c < kNumGenericCfgs; ++c) {
+    const GenericCfg& g = kGenericCfgs[c];
+    const GenericCfg& b = kGenericCfgs[best];
+    const int64_t cg = generic_cost(g, M, N, cu), cb = generic_cost(b, M, N, cu);
+    const int wg = g.waves_m * g.waves_n, wb = b.waves_m * b.waves_n;
+    if (cg < cb || (cg == cb && (g.bm * g.bn > b.bm * b.bn || (g.bm * g.bn == b.bm * b.bn && wg > wb)))) best = c;
+  }
+  return best;
+}
+
+// Split K until the grid covers the device once, keeping at least one group
+// per wave in every split.
+int64_t swap_split(const SkinnyCfg& k, int64_t tiles, int64_t G, int cu) {
+  const int64_t want = cdiv(cu, tiles);
+  const int64_t cap = G / k.kw > 1 ? G / k.kw : 1;
+  const int64_t S = want < cap ? want : cap;
+  return S < 1 ? 1 : S;
+}
+
+// The swap-AB kernels' cost in the units of generic_cost x groups: per-CU
+// rows x groups, weighted 3/2 because their direct-to-register loads were
+// measured ~1.4x slower per byte than the generic kernel's LDS DMA, plus
+// the split-K handshake (~1.3 us, about 32 rows x 8 groups at the measured
+// rate) when K is split.
+int64_t swap_cost(int64_t M, int64_t N, int64_t G, int cu) {
+  const SkinnyCfg& k = kSwapCfgs[swap_cfg_for(M, N, cu)];
+  const int64_t tiles = skinny_tiles(k, M, N);
+  const int64_t S = swap_split(k, tiles, G, cu);
+  const int64_t rows = skinny_tile_m(k) + skinny_tile_n(k);
+  return cdiv(tiles * S, cu) * rows * cdiv(G, S) * 3 / 2 + (S > 1 ? 256 : 0);
 }
 
 }  // namespace
@@ -94,12 +130,17 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
 
   int v = variant;
   if (v == FBG_VARIANT_AUTO) {
-    // Swap-AB (maybe split over K below) for M <= 64, and up to M = 128 when
-    // the generic kernel's smallest tile would leave over half the device idle.
+    // Swap-AB (maybe split over K) for M <= 16; the generic kernel above
+    // M = 128; in between, whichever pulls fewer bytes per CU by the cost
+    // model of generic_cost / swap_cost.
     if (K == 256 && M <= 1024)
       v = FBG_VARIANT_SHORT_K256;
-    else if (M <= 64 || (M <= 128 && cdiv(M, 64) * cdiv(N, 128) < (int64_t)cu / 2))
+    else if (M <= 16)
       v = FBG_VARIANT_SWAP_AB;
+    else if (M <= 128)
+      v = generic_cost(kGenericCfgs[generic_cfg_for(M, N, cu)], M, N, cu) * G <= swap_cost(M, N, G, cu)
+              ? FBG_VARIANT_GENERIC
+              : FBG_VARIANT_SWAP_AB;
     else
       v = FBG_VARIANT_GENERIC;
   }
@@ -134,12 +175,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
     if (split_k > 0) {
       S = split_k;
     } else if (variant == FBG_VARIANT_AUTO || variant == FBG_VARIANT_SWAP_AB_SPLITK) {
-      // Split K until the grid covers the device once, keeping at least one
-      // group per wave in every split.
-      const int64_t want = cdiv(cu, tiles);
-      const int64_t cap = G / k.kw > 1 ? G / k.kw : 1;
-      S = want < cap ? want : cap;
-      if (S < 1) S = 1;
+      S = swap_split(k, tiles, G, cu);
     }
     if (variant == FBG_VARIANT_AUTO) v = S > 1 ? FBG_VARIANT_SWAP_AB_SPLITK : FBG_VARIANT_SWAP_AB;
     out->variant = v;
@@ -168,19 +204,23 @@ int64_t workspace_bytes(const fbg_plan& p, int64_t M, int64_t N) {
   return workspace_counter_offset(p, M, N) + T * 4;
 }
 
-// Grouped: by the mean number of tokens per expert -- 32 n x 16 m tiles
-// (config 0) for decode-sized groups, 32 n x 32 m (config 1) up to 32, and
-// 32 n x 64 m (config 2) above, so each expert's weight rows are streamed
-// once per few token tiles.  force_cfg >= 0 picks a configuration; -1 is
-// returned for one that does not exist.
+// Grouped: by the mean number of tokens per expert (measured on 256 experts
+// of 512 x 4096, 16 .. 1024 tokens routed top-8).  Up to 12: 32-column tiles
+// of one 16-row block with the K range split over 8 waves (config 5: the
+// weight stream is the whole cost, and 8 waves keep the most loads in
+// flight); up to 20: 32 x 32 tiles (config 1); above: 64-column tiles of up
+// to 64 rows (config 6), which cut the activation re-reads (one per column
+// tile) 2x and stream each weight tile once for experts of up to 64 tokens.
+// Tiles compute only their 16-row blocks that hold tokens.  force_cfg >= 0
+// picks a configuration; -1 is returned for one that does not exist.
 int grouped_cfg_for(int64_t M, int64_t E, int64_t N, int64_t K, int force_cfg) {
   (void)N;
   (void)K;
   if (force_cfg >= 0) return force_cfg < kNumGroupedCfgs ? force_cfg : -1;
   const int64_t per = E > 0 ? cdiv(M, E) : M;
-  if (per <= 16) return 0;
-  if (per <= 32) return 1;
-  return 2;
+  if (per <= 12) return 5;
+  if (per <= 20) return 1;
+  return 6;
 }
 
 int64_t grouped_grid(int cfg, int64_t E, int64_t N) {
@@ -192,6 +232,23 @@ int64_t grouped_grid(int cfg, int64_t E, int64_t N) {
 extern "C" int fp8_block_gemm_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int variant,
                                    int split_k, fbg_plan* out) {
   return fbg::make_plan(M, N, K, out_dtype, cu_count, variant, split_k, out, -1);
+}
+
+extern "C" int fp8_block_gemm_grouped_plan(int64_t E, int64_t M, int64_t N, int64_t K, fbg_plan* out) {
+  if (!out || E < 0 || M < 0 || N < 0 || K < 0) return FBG_ERROR_INVALID_VALUE;
+  if (K % 128 != 0) return FBG_ERROR_UNSUPPORTED;
+  const int cfg = fbg::grouped_cfg_for(M, E, N, K, -1);
+  const fbg::SkinnyCfg& k = fbg::kGroupedCfgs[cfg];
+  memset(out, 0, sizeof(*out));
+  out->variant = FBG_VARIANT_GROUPED;
+  out->tile_m = fbg::skinny_tile_m(k);
+  out->tile_n = fbg::skinny_tile_n(k);
+  out->split_k = 1;
+  out->waves = k.kw;
+  out->config = cfg;
+  out->grid = fbg::grouped_grid(cfg, E, N);
+  out->workspace_bytes = 0;
+  return FBG_SUCCESS;
 }
 
 extern "C" const char* fp8_block_gemm_status_string(int status) {

@@ -58,7 +58,8 @@ enum {
     FBG_VARIANT_GENERIC = 1,       /* LDS-staged MFMA tiles, any shape */
     FBG_VARIANT_SHORT_K256 = 2,    /* K == 256: both groups unrolled, a_s*b_s pre-folded */
     FBG_VARIANT_SWAP_AB = 3,       /* C^T = B A^T: weight rows on the 16-row MFMA side, small M on the other */
-    FBG_VARIANT_SWAP_AB_SPLITK = 4 /* swap-AB with K split over workgroups, fixed-order FP32 reduction */
+    FBG_VARIANT_SWAP_AB_SPLITK = 4, /* swap-AB with K split over workgroups, fixed-order FP32 reduction */
+    FBG_VARIANT_GROUPED = 5        /* reported by fp8_block_gemm_grouped_plan only; not a forcible variant */
 };
 
 /* One dispatcher decision (pure data, filled by fp8_block_gemm_plan). */
@@ -154,6 +155,17 @@ int fp8_block_gemm_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_c
 int fp8_block_gemm_grouped(const void *A, const float *a_s, const void *B, const float *b_s, void *C,
                            const int32_t *offsets, int64_t E, int64_t M, int64_t N, int64_t K,
                            int out_dtype, void *stream);
+
+/*
+ * fp8_block_gemm_grouped_plan -- the tile configuration fp8_block_gemm_grouped
+ * uses for E experts holding M token rows in total (chosen by the mean rows
+ * per expert), as a plan: variant FBG_VARIANT_GROUPED, tile_m = the most
+ * token rows a tile holds (a tile computes only its 16-row blocks that hold
+ * tokens), tile_n, waves, config, grid = E * ceil(N / tile_n) workgroups
+ * (those of empty experts exit at once), split_k 1, no workspace.  Pure host
+ * code.  Negative sizes -> INVALID_VALUE; K % 128 != 0 -> UNSUPPORTED.
+ */
+int fp8_block_gemm_grouped_plan(int64_t E, int64_t M, int64_t N, int64_t K, fbg_plan *out);
 
 /*
  * fp8_block_gemm_quantize_rows -- the producer of A and a_s: per-token 1x128

@@ -256,3 +256,19 @@ def test_grouped_wrapper_checks():
         fbg.grouped_gemm(A, a_s, B[0], b_s, torch.zeros(3, dtype=torch.int32))
     with pytest.raises(ValueError):
         fbg.grouped_gemm(A, a_s, B, torch.zeros((2, 1, 2)), torch.zeros(3, dtype=torch.int32))
+
+
+def test_grouped_plan():
+    for E, M, N in [(256, 128, 512), (256, 512, 512), (256, 8192, 512), (7, 100, 300), (1, 5, 130)]:
+        p = fbg.grouped_plan(E, M, N, 1024)
+        assert p["variant_name"] == "grouped" and p["split_k"] == 1 and p["workspace_bytes"] == 0
+        assert p["grid"] == E * -(-N // p["tile_n"])
+        assert 128 % p["tile_n"] == 0 and p["tile_m"] % 16 == 0
+    # more tokens per expert -> taller tiles
+    assert fbg.grouped_plan(256, 8192, 512, 4096)["tile_m"] > fbg.grouped_plan(256, 512, 512, 4096)["tile_m"]
+    with pytest.raises(fbg.FP8BGError) as e:
+        fbg.grouped_plan(-1, 5, 130, 256)
+    assert e.value.status == fbg.INVALID_VALUE
+    with pytest.raises(fbg.FP8BGError) as e:
+        fbg.grouped_plan(2, 5, 130, 200)
+    assert e.value.status == fbg.UNSUPPORTED

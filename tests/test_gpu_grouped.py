@@ -41,6 +41,16 @@ GROUPED_CASES = [
     (4, [2, 2, 2], 257, 2048),
     (5, [3, 0, 17, 40], 300, 4096),
     (5, [100, 1], 130, 1152),
+    (6, [3, 0, 17, 40, 64, 65, 130], 300, 4096),
+    (6, [5, 1, 0, 33], 257, 1152),
+    (7, [9, 0, 20, 1, 32, 33], 130, 2048),
+    (7, [33, 2], 300, 640),
+    (8, [12, 0, 3, 30, 48, 49], 515, 1024),
+    (8, [1, 70], 140, 384),
+    (9, [7, 0, 40, 64, 100], 600, 4096),
+    (9, [2, 17, 50], 130, 1024),
+    (10, [7, 0, 40, 31], 600, 2048),
+    (10, [16, 17], 260, 1024),
 ]
 
 

@@ -31,6 +31,14 @@ TOL_CASES = [
     ("generic", 2, 1, 130, 128, 0),
     ("generic", 3, 300, 520, 640, 0),
     ("generic", 3, 513, 257, 256, 0),
+    ("generic", 4, 200, 300, 1024, 0),
+    ("generic", 4, 64, 130, 512, 0),
+    ("generic", 4, 1, 100, 256, 0),
+    ("generic", 5, 300, 200, 1024, 0),
+    ("generic", 5, 65, 515, 384, 0),
+    ("generic", 6, 130, 300, 1024, 0),
+    ("generic", 6, 64, 33, 256, 0),
+    ("generic", 6, 129, 260, 640, 0),
     ("short_k256", 0, 184, 700, 256, 0),
     ("short_k256", 0, 300, 515, 256, 0),
     ("short_k256", 1, 37, 130, 256, 0),

@@ -189,6 +189,12 @@ class MoEWorkload:
 MOE_WORKLOADS = {
     "moe_decode_t64_e256_512x4096": MoEWorkload("moe_decode_t64_e256_512x4096", 64, 256, 8, 512, 4096, seed=11,
                                                 note="MoE decode: 64 tokens, top-8 of 256 experts, expert weight 512x4096"),
+    "moe_t16_e256_512x4096": MoEWorkload("moe_t16_e256_512x4096", 16, 256, 8, 512, 4096, seed=12,
+                                         note="16 tokens: about half the experts hold a row"),
+    "moe_t256_e256_512x4096": MoEWorkload("moe_t256_e256_512x4096", 256, 256, 8, 512, 4096, seed=13,
+                                          note="256 tokens: 8 rows per expert on average"),
+    "moe_t1024_e256_512x4096": MoEWorkload("moe_t1024_e256_512x4096", 1024, 256, 8, 512, 4096, seed=14,
+                                           note="1024 tokens: 32 rows per expert on average"),
 }
 
 
