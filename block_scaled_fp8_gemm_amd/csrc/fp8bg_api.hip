@@ -250,7 +250,7 @@ extern "C" int fp8_block_gemm_grouped(const void* A, const float* a_s, const voi
     return fbg::launch_fill_zero(C, M * N, out_dtype, stream) == hipSuccess ? FBG_SUCCESS : FBG_ERROR_HIP;
   const int cfg = fbg::grouped_cfg_for(M, E, N, K, forced_config());
   if (cfg < 0) return FBG_ERROR_UNSUPPORTED;
-  const int64_t grid = fbg::grouped_grid(cfg, E, N);
+  const int64_t grid = fbg::grouped_grid(cfg, E, M, N);
   if (grid > INT32_MAX) return FBG_ERROR_UNSUPPORTED;
 
   fbg::GemmArgs args;
@@ -268,6 +268,9 @@ extern "C" int fp8_block_gemm_grouped(const void* A, const float* a_s, const voi
   if (env_flag("FBG_LOG"))
     fprintf(stderr, "fp8bg grouped: E=%lld M=%lld N=%lld K=%lld out=%d -> cfg=%d grid=%lld\n", (long long)E,
             (long long)M, (long long)N, (long long)K, out_dtype, cfg, (long long)grid);
-  const hipError_t e = fbg::launch_grouped(args, cfg, grid, offsets, (int)E);
+  const hipError_t e = cfg < fbg::grouped_num_skinny_cfgs()
+                           ? fbg::launch_grouped(args, cfg, grid, offsets, (int)E)
+                           : fbg::launch_generic_grouped(args, cfg - fbg::grouped_num_skinny_cfgs(), grid, offsets,
+                                                         (int)E);
   return e == hipSuccess ? FBG_SUCCESS : FBG_ERROR_HIP;
 }

@@ -18,6 +18,41 @@
 
 namespace fbg {
 
+// Grouped form of the generic kernel: row tile t (in expert order, expert e
+// holding ceil(rows_e / BM) tiles) -> (expert, tile within the expert),
+// written to out[0..1] by one wave; out[0] = -1 if t is past the last tile.
+// The wave scans the experts' tile counts 64 at a time (offsets clamped into
+// [0, M] as everywhere else), so no host step or extra launch is needed.
+template <int BM>
+__device__ __forceinline__ void find_expert_tile(const int* offsets, int E, int M, int t, int lane, int* out) {
+  int carry = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    int tiles = 0;
+    if (e < E) {
+      int lo = offsets[e], hi = offsets[e + 1];
+      lo = lo < 0 ? 0 : (lo > M ? M : lo);
+      hi = hi < lo ? lo : (hi > M ? M : hi);
+      tiles = (hi - lo + BM - 1) / BM;
+    }
+    int incl = tiles;  // inclusive prefix sum over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const int first = carry + incl - tiles;
+    const bool mine = tiles > 0 && t >= first && t < first + tiles;
+    if (mine) {
+      out[0] = e;
+      out[1] = t - first;
+    }
+    if (__any(mine)) return;
+    carry += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) out[0] = -1;
+}
+
 // ===========================================================================
 // Generic kernel: LDS-staged A and B tiles, STAGES-deep ring, one 128-wide
 // group per step.  (The pages' generic tuned GEMM and its GROUP_M raster,
@@ -43,10 +78,11 @@ namespace fbg {
 // Each MFMA writes a fresh FP32 partial; its fold acc = fma(P, s, acc) is
 // issued after the next MFMA, in that MFMA's shadow.
 // ===========================================================================
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int OUT>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int OUT, int GRP>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
     const uint8_t* __restrict__ A, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
-    const float* __restrict__ b_s, void* __restrict__ C, int M, int N, int K, int band, int vec_ok) {
+    const float* __restrict__ b_s, void* __restrict__ C, int M, int N, int K, int band, int vec_ok,
+    const int* __restrict__ offsets, int E) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -68,11 +104,35 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int G = K / kGroup;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tm, tn;
-  raster(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, band, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int tiles_n = (N + BN - 1) / BN;
   const int nblk = (N + 127) / 128;
+  int m0, n0, m_end;  // the tile's first row, first column, and the end of its rows
+  if constexpr (GRP) {
+    // Grouped: the grid enumerates (row tile t, column tile tn) with t over
+    // the experts' row tiles in expert order, ceil(rows_e / BM) per expert.
+    __shared__ int sTile[2];
+    const int lid = xcd_remap(blockIdx.x, (int)gridDim.x);
+    const int t = lid / tiles_n, tn = lid - t * tiles_n;
+    if (wave == 0) find_expert_tile<BM>(offsets, E, M, t, lane, sTile);
+    __syncthreads();
+    const int e = sTile[0];
+    if (e < 0) return;  // past the last row tile (uniform over the workgroup)
+    int lo = offsets[e], hi = offsets[e + 1];
+    lo = lo < 0 ? 0 : (lo > M ? M : lo);
+    hi = hi < lo ? lo : (hi > M ? M : hi);
+    m0 = lo + sTile[1] * BM;
+    m_end = hi;
+    n0 = tn * BN;
+    B += (int64_t)e * N * K;
+    b_s += (int64_t)e * nblk * G;
+  } else {
+    const int tiles_m = (M + BM - 1) / BM;
+    int tm, tn;
+    raster(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, band, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+    m_end = M;
+  }
   const int nb = ((n0 + wn * WN) >> 7) < nblk ? ((n0 + wn * WN) >> 7) : nblk - 1;
 
   // Per-lane 32-bit source offsets inside the tile's rows (rows past the
@@ -86,7 +146,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 #pragma unroll
   for (int i = 0; i < A_PER_T; ++i) {
     const int r = 8 * (i * NW + wave) + (lane >> 3);
-    const int gr = (m0 + r) < M ? r : (M - 1 - m0);
+    const int gr = (m0 + r) < m_end ? r : (m_end - 1 - m0);
     aoff[i] = (uint32_t)gr * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ swz_row(r));
   }
 #pragma unroll
@@ -101,7 +161,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   // (64w mod BM) + lane.
   const int slot = (wave * 64) % BM + lane;
   const int srow = (slot / (16 * IB)) * WM + 16 * (slot % IB) + (slot / IB) % 16;
-  const int sr = (m0 + srow) < M ? (m0 + srow) : (M - 1);
+  const int sr = (m0 + srow) < m_end ? (m0 + srow) : (m_end - 1);
   const uint32_t soff = (uint32_t)sr * (uint32_t)G * 4u;
   // b_s of the tile's column blocks (lane l holds block n0/128 + l, clamped),
   // so the loop issues no scalar-memory loads.
@@ -237,7 +297,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
     for (int j = 0; j < JB; ++j) {
       const int m = m_l + 16 * i, n = n_l + 16 * j;
       const int cnt = (N - n) < 4 ? (N - n) : 4;
-      if (m < M && cnt > 0) store4<OUT>(C, (int64_t)m * N + n, acc[i][j], cnt, vec_ok);
+      if (m < m_end && cnt > 0) store4<OUT>(C, (int64_t)m * N + n, acc[i][j], cnt, vec_ok);
     }
 }
 
@@ -643,21 +703,21 @@ __global__ void k_fill_zero(void* __restrict__ C, int64_t count) {
 // ===========================================================================
 // Launchers
 // ===========================================================================
-template <int BM, int BN, int WM_, int WN_, int ST>
-static hipError_t launch_generic_t(const GemmArgs& a, int64_t grid, int band) {
+template <int BM, int BN, int WM_, int WN_, int ST, int GRP>
+static hipError_t launch_generic_t(const GemmArgs& a, int64_t grid, int band, const int* offsets, int E) {
   const dim3 blk(64 * WM_ * WN_);
   switch (a.out) {
     case kOutBF16:
-      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutBF16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
-                         a.b_s, a.C, a.M, a.N, a.K, band, a.vec);
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutBF16, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+                         a.B, a.b_s, a.C, a.M, a.N, a.K, band, a.vec, offsets, E);
       break;
     case kOutFP16:
-      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutFP16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
-                         a.b_s, a.C, a.M, a.N, a.K, band, a.vec);
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutFP16, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+                         a.B, a.b_s, a.C, a.M, a.N, a.K, band, a.vec, offsets, E);
       break;
     default:
-      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutFP32>), dim3(grid), blk, 0, a.stream, a.A, a.a_s, a.B,
-                         a.b_s, a.C, a.M, a.N, a.K, band, a.vec);
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutFP32, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+                         a.B, a.b_s, a.C, a.M, a.N, a.K, band, a.vec, offsets, E);
   }
   return hipGetLastError();
 }
@@ -665,7 +725,17 @@ static hipError_t launch_generic_t(const GemmArgs& a, int64_t grid, int band) {
 hipError_t launch_generic(const GemmArgs& a, int cfg, int64_t grid, int band) {
   switch (cfg) {
 #define X(id, bm, bn, wm, wn, st) \
-  case id: return launch_generic_t<bm, bn, wm, wn, st>(a, grid, band);
+  case id: return launch_generic_t<bm, bn, wm, wn, st, 0>(a, grid, band, nullptr, 0);
+    FBG_GENERIC_CFGS(X)
+#undef X
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_generic_grouped(const GemmArgs& a, int cfg, int64_t grid, const int* offsets, int E) {
+  switch (cfg) {
+#define X(id, bm, bn, wm, wn, st) \
+  case id: return launch_generic_t<bm, bn, wm, wn, st, 1>(a, grid, 0, offsets, E);
     FBG_GENERIC_CFGS(X)
 #undef X
     default: return hipErrorInvalidValue;

@@ -143,10 +143,14 @@ int fp8_block_gemm_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_c
  * (expert e's weight at B + e*N*K), b_s [E, ceil(N/128), K/128] fp32.
  * offsets: DEVICE pointer to E+1 int32, non-decreasing, offsets[0] = 0,
  * offsets[E] = M (typically written by the router on the GPU, so the call
- * never synchronises with the host).  The kernel clamps every offset into
- * [0, M]: malformed offsets can leave rows of C unwritten but never make it
- * read or write outside A, a_s or C.  Rows of C outside every expert's
- * range are not written.  M, N, K, E >= 0 with K % 128 == 0; M == 0 or
+ * never synchronises with the host).  The kernels clamp every offset into
+ * [0, M]: malformed offsets can leave rows of C unwritten (or, for ranges
+ * that overlap, written by more than one expert) but never make a kernel
+ * read or write outside A, a_s, B, b_s or C.  Rows of C outside every
+ * expert's range are not written.  Small experts run on skinny swap-AB
+ * tiles (one workgroup per expert and column tile); prefill-sized experts
+ * on the LDS-staged generic kernel, whose workgroups find their expert and
+ * row tile with a scan of the offsets on the device.  M, N, K, E >= 0 with K % 128 == 0; M == 0 or
  * N == 0: nothing launched; K == 0 or E == 0: C is filled with zeros.
  * Alignment as for fp8_block_gemm, offsets 4-byte aligned; statuses as for
  * fp8_block_gemm (C overlapping any input -> INVALID_VALUE).  No workspace;

@@ -166,7 +166,10 @@ def test_every_tile_configuration_has_parity_cases():
     assert ids("FBG_SWAP_CFGS") <= have["swap_ab"]
     assert ids("FBG_SHORT_CFGS") <= have["short_k256"]
     from tests.test_gpu_grouped import GROUPED_CASES
-    assert ids("FBG_GROUPED_CFGS") <= {c[0] for c in GROUPED_CASES}
+    grouped = {c[0] for c in GROUPED_CASES}
+    n_skinny = len(ids("FBG_GROUPED_CFGS"))
+    assert ids("FBG_GROUPED_CFGS") <= grouped
+    assert {n_skinny + c for c in ids("FBG_GENERIC_CFGS")} <= grouped     # the generic kernel in grouped mode
 
 
 def _qcall(x=0x100000, M=4, K=256, A=0x200000, a_s=0x300000):
@@ -259,13 +262,18 @@ def test_grouped_wrapper_checks():
 
 
 def test_grouped_plan():
-    for E, M, N in [(256, 128, 512), (256, 512, 512), (256, 8192, 512), (7, 100, 300), (1, 5, 130)]:
+    for E, M, N in [(256, 128, 512), (256, 512, 512), (256, 8192, 512), (7, 100, 300), (1, 5, 130)]:  # skinny
         p = fbg.grouped_plan(E, M, N, 1024)
         assert p["variant_name"] == "grouped" and p["split_k"] == 1 and p["workspace_bytes"] == 0
         assert p["grid"] == E * -(-N // p["tile_n"])
         assert 128 % p["tile_n"] == 0 and p["tile_m"] % 16 == 0
-    # more tokens per expert -> taller tiles
+    # more tokens per expert -> taller tiles; prefill-sized experts on the
+    # generic kernel, whose grid bounds the experts' row tiles by
+    # ceil(M / BM) + E
     assert fbg.grouped_plan(256, 8192, 512, 4096)["tile_m"] > fbg.grouped_plan(256, 512, 512, 4096)["tile_m"]
+    p = fbg.grouped_plan(256, 32768, 512, 4096)
+    assert p["tile_m"] == 256 and p["waves"] == 8
+    assert p["grid"] == (-(-32768 // 256) + 256) * -(-512 // p["tile_n"])
     with pytest.raises(fbg.FP8BGError) as e:
         fbg.grouped_plan(-1, 5, 130, 256)
     assert e.value.status == fbg.INVALID_VALUE

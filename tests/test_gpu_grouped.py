@@ -53,6 +53,28 @@ GROUPED_CASES = [
     (10, [16, 17], 260, 1024),
 ]
 
+# The generic kernel in grouped mode: configuration 11 + c runs generic tile
+# configuration c (BM x BN: 0 128x128, 1 256x128, 2 64x128, 3 256x256,
+# 4 64x64, 5 128x64, 6 64x32).  Experts spanning several row tiles, empty
+# experts, more than 64 experts (the tile scan's second chunk), ragged N.
+GENERIC_GROUPED_CASES = [
+    (11, [130, 0, 1, 300, 7], 300, 1024),
+    (11, [3] * 70 + [200], 130, 256),
+    (12, [513, 0, 40], 260, 512),
+    (12, [1, 257, 256], 130, 384),
+    (13, [65, 0, 64, 129, 3], 515, 1024),
+    (13, [5] * 100, 200, 256),
+    (14, [300, 1, 0, 257], 600, 640),
+    (14, [256, 256], 257, 256),
+    (15, [65, 0, 64, 129, 3], 300, 2048),
+    (15, [1] * 130, 140, 256),
+    (16, [129, 0, 128, 1, 200], 260, 1024),
+    (16, [7, 0, 0, 300], 130, 384),
+    (17, [65, 0, 64, 129, 3], 300, 1024),
+    (17, [2] * 66, 130, 512),
+]
+GROUPED_CASES = GROUPED_CASES + GENERIC_GROUPED_CASES
+
 
 def to_dev(d):
     return {
@@ -133,7 +155,8 @@ def test_moe_decode_size_sampled_rows(gpu):
         assert np.all(np.abs(got[m:m + 1] - ref) <= tol), f"row {m} (expert {e})"
 
 
-def test_rows_outside_every_expert_are_untouched_and_offsets_are_clamped(gpu):
+@pytest.mark.parametrize("cfg", [None, 11, 14])
+def test_rows_outside_every_expert_are_untouched_and_offsets_are_clamped(gpu, cfg):
     """Offsets are device data the kernel clamps into [0, M]: rows no expert
     holds keep the caller's values, offsets past M are cut at M, decreasing
     pairs are empty."""
@@ -144,13 +167,13 @@ def test_rows_outside_every_expert_are_untouched_and_offsets_are_clamped(gpu):
     # expert 0 holds rows [0,4); expert 1's pair decreases (4 -> 2) and
     # expert 2's is empty (2 -> 2): rows 4.. are held by no expert
     dd["offsets"] = torch.tensor([0, 4, 2, 2], dtype=torch.int32, device=DEV)
-    C = run(dd, "fp32", C=sentinel.clone())
+    C = run(dd, "fp32", cfg, C=sentinel.clone())
     ref = oracle.block_gemm(d["A"][0:4], d["a_s"][0:4], d["B"][0], d["b_s"][0])
     assert_within_tolerance(C[:4], ref, "fp32", "held rows")
     assert torch.equal(C[4:], sentinel[4:])
     # the last offset past M: the last expert's rows end at M
     dd["offsets"] = torch.tensor([0, 4, 10, 1000], dtype=torch.int32, device=DEV)
-    C = run(dd, "fp32", C=sentinel.clone())
+    C = run(dd, "fp32", cfg, C=sentinel.clone())
     ref = np.empty((M, N))
     for e, (r0, r1) in enumerate([(0, 4), (4, 10), (10, 13)]):
         ref[r0:r1] = oracle.block_gemm(d["A"][r0:r1], d["a_s"][r0:r1], d["B"][e], d["b_s"][e])
