@@ -406,6 +406,16 @@ def main():
                         f.write(json.dumps(line) + "\n")
                         f.flush()
                         print(json.dumps(line), flush=True)
+            for name, mw in W.MOE_WORKLOADS.items():   # the grouped (MoE) GEMM
+                r = run_grouped(args, mw, torch, fbg, W, 400, 20, not args.no_graph)
+                line = {"op": "grouped", "workload": name, "tokens": mw.tokens, "experts": mw.experts,
+                        "top_k": mw.top_k, "rows": r["M"], "N": mw.N, "K": mw.K, "cfg": r["cfg"],
+                        "active_experts": int((r["d"]["offsets"][1:] > r["d"]["offsets"][:-1]).sum()),
+                        "us": round(r["ms_per_step"] * 1e3, 3), "tflops": round(r["tflops"], 2),
+                        "gbs": round(r["gbs"], 1), "roofline": r["roof"], "copies": r["copies"]}
+                f.write(json.dumps(line) + "\n")
+                f.flush()
+                print(json.dumps(line), flush=True)
             for name, w in W.WORKLOADS.items():     # the activation quantiser on each workload's A
                 r = run_quantize(args, w, w.M, torch, fbg, 200 if w.M * w.K > 1e7 else 2048, 20, not args.no_graph)
                 line = {"op": "quantize", "workload": name, "M": w.M, "K": w.K,
