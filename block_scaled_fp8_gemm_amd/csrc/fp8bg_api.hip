@@ -67,6 +67,8 @@ int validate(const void* A, const float* a_s, const void* B, const float* b_s, c
   const int64_t G = K / 128, NB = (N + 127) / 128;
   const int64_t bytesA = M * K, bytesB = N * K, bytesAs = M * G * 4, bytesBs = NB * G * 4;
   const int64_t bytesC = M * N * elem_size(out_dtype);
+  // The generic kernel addresses the scale arrays with 32-bit buffer offsets.
+  if (bytesAs > (int64_t)UINT32_MAX || bytesBs > (int64_t)UINT32_MAX) return FBG_ERROR_UNSUPPORTED;
   if ((bytesA > 0 && !A) || (bytesB > 0 && !B) || (bytesAs > 0 && !a_s) || (bytesBs > 0 && !b_s) ||
       (bytesC > 0 && !C))
     return FBG_ERROR_INVALID_VALUE;
@@ -232,8 +234,13 @@ extern "C" int fp8_block_gemm_grouped(const void* A, const float* a_s, const voi
   if (K % 128 != 0) return FBG_ERROR_UNSUPPORTED;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || E > INT32_MAX - 1) return FBG_ERROR_UNSUPPORTED;
   const int64_t G = K / 128, NB = (N + 127) / 128;
-  const int64_t bytesA = M * K, bytesAs = M * G * 4, bytesB = E * N * K, bytesBs = E * NB * G * 4;
+  int64_t bytesB = 0, bytesBs = 0;
+  if (__builtin_mul_overflow(E, N * K, &bytesB) || __builtin_mul_overflow(E, NB * G * 4, &bytesBs))
+    return FBG_ERROR_UNSUPPORTED;  // B or b_s larger than any address space
+  const int64_t bytesA = M * K, bytesAs = M * G * 4;
   const int64_t bytesC = M * N * elem_size(out_dtype), bytesOff = (E + 1) * 4;
+  // The generic kernel addresses the scale arrays (one expert's b_s) with 32-bit buffer offsets.
+  if (bytesAs > (int64_t)UINT32_MAX || NB * G * 4 > (int64_t)UINT32_MAX) return FBG_ERROR_UNSUPPORTED;
   if ((bytesA > 0 && !A) || (bytesAs > 0 && !a_s) || (bytesB > 0 && !B) || (bytesBs > 0 && !b_s) ||
       (bytesC > 0 && !C) || (E > 0 && !offsets))
     return FBG_ERROR_INVALID_VALUE;

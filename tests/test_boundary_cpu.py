@@ -245,6 +245,9 @@ def test_grouped_host_validation_statuses():
     assert _gcall(C=0x600000 - 64) == fbg.INVALID_VALUE     # C overlaps the offsets
     assert _gcall(M=0, A=None, a_s=None, C=None) == fbg.SUCCESS   # empty: nothing launched
     assert _gcall(N=0, B=None, b_s=None, C=None) == fbg.SUCCESS
+    assert _gcall(E=1 << 30, N=1 << 30, K=1 << 30) == fbg.UNSUPPORTED   # E*N*K overflows int64
+    assert _gcall(M=1 << 31) == fbg.UNSUPPORTED                          # above INT32_MAX
+    assert _call(M=(1 << 31) - 1, K=1 << 20) == fbg.UNSUPPORTED          # a_s of 64 GiB: past 32-bit offsets
 
 
 def test_grouped_wrapper_checks():
