@@ -283,3 +283,28 @@ def test_grouped_plan():
     with pytest.raises(fbg.FP8BGError) as e:
         fbg.grouped_plan(2, 5, 130, 200)
     assert e.value.status == fbg.UNSUPPORTED
+
+
+def test_header_is_plain_c_and_matches_the_library(tmp_path):
+    """include/fp8bg.h compiles as C99 and C++ on its own, and a C program
+    that calls every declared function's address links against the library
+    (signatures as declared, C linkage)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    names = declared_functions()
+    src = tmp_path / "use.c"
+    src.write_text('#include "fp8bg.h"\n#include <stdio.h>\nint main(void) {\n'
+                   + "".join(f'  printf("%p\\n", (void *)&{n});\n' for n in names)
+                   + "  fbg_plan p;\n  return fp8_block_gemm_plan(64, 512, 4096, FBG_OUT_BF16, 256, FBG_VARIANT_AUTO, 0, &p)"
+                     " == FBG_SUCCESS && p.split_k >= 1 ? 0 : 1;\n}\n")
+    lib = os.path.join(ROOT, "block_scaled_fp8_gemm_amd")
+    exe = tmp_path / "use"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-L", lib, "-lfp8bg", "-Wl,-rpath," + lib, "-o", str(exe)], check=True)
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-fsyntax-only", "-x", "c++",
+                    "-I", os.path.join(ROOT, "include"), str(src)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert len(r.stdout.split()) == len(names)
