@@ -164,7 +164,7 @@ extern "C" int fp8_block_gemm_ex(const void* A, const float* a_s, const void* B,
     return FBG_ERROR_OUT_OF_MEMORY;
   }
   const int64_t coff = fbg::workspace_counter_offset(p, M, N);
-  if (hipMemsetAsync(static_cast<char*>(ws) + coff, 0, (size_t)(p.workspace_bytes - coff), stream) != hipSuccess) {
+  if (fbg::launch_zero_words(static_cast<char*>(ws) + coff, (p.workspace_bytes - coff) / 4, stream) != hipSuccess) {
     (void)hipFreeAsync(ws, stream);
     return FBG_ERROR_HIP;
   }

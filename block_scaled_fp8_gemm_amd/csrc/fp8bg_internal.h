@@ -48,6 +48,7 @@ struct GemmArgs {
 hipError_t launch_generic(const GemmArgs& a, int cfg, int64_t grid, int band);
 hipError_t launch_swap(const GemmArgs& a, int cfg, int64_t grid, int S, float* ws, unsigned* counters);
 hipError_t launch_short_k256(const GemmArgs& a, int cfg, int64_t grid);
+hipError_t launch_zero_words(void* p, int64_t count, hipStream_t stream);
 hipError_t launch_fill_zero(void* C, int64_t count, int out, hipStream_t stream);
 hipError_t launch_grouped(const GemmArgs& a, int cfg, int64_t grid, const int* offsets, int E);
 hipError_t launch_generic_grouped(const GemmArgs& a, int cfg, int64_t grid, const int* offsets, int E);

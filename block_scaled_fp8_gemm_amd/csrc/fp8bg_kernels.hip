@@ -810,6 +810,22 @@ hipError_t launch_grouped(const GemmArgs& a, int cfg, int64_t grid, const int* o
   }
 }
 
+// Zeroes `count` 32-bit words with plain vector stores (the split-K arrival
+// counters of a fresh workspace).  A kernel rather than hipMemsetAsync, so a
+// caller may capture the call in a HIP graph.
+__global__ void k_zero_words(uint32_t* __restrict__ p, int64_t count) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(void* p, int64_t count, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  const int64_t blocks64 = (count + 255) / 256;
+  const unsigned blocks = (unsigned)(blocks64 < 1024 ? blocks64 : 1024);
+  hipLaunchKernelGGL(k_zero_words, dim3(blocks), dim3(256), 0, stream, static_cast<uint32_t*>(p), count);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(void* C, int64_t count, int out, hipStream_t stream) {
   const int64_t blocks64 = (count + 255) / 256;
   const unsigned blocks = (unsigned)(blocks64 < 4096 ? (blocks64 > 0 ? blocks64 : 1) : 4096);

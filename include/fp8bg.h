@@ -86,7 +86,9 @@ typedef struct fbg_plan {
  * of 4 GiB or more -> UNSUPPORTED.  When the chosen kernel splits
  * K, its FP32 workspace is taken from a stream-ordered allocation on `stream`
  * (hipMallocAsync / hipFreeAsync), so concurrent calls on different streams
- * do not share it; failure -> OUT_OF_MEMORY before anything is launched.
+ * do not share it; failure -> OUT_OF_MEMORY before anything is launched.  Its
+ * arrival counters are zeroed by a small kernel (no hipMemsetAsync), so the
+ * call may be captured in a HIP graph as it is.
  */
 int fp8_block_gemm(const void *A, const float *a_s, const void *B, const float *b_s,
                    void *C, int64_t M, int64_t N, int64_t K, int out_dtype, void *stream);
