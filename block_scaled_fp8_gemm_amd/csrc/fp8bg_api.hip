@@ -81,11 +81,19 @@ int validate(const void* A, const float* a_s, const void* B, const float* b_s, c
   return FBG_SUCCESS;
 }
 
+// FBG_RASTER_BAND=<rows>: benchmarks try other raster band heights for the
+// generic kernel (default 8 tile-rows).
+int raster_band() {
+  const char* v = getenv("FBG_RASTER_BAND");
+  const int b = (v && v[0]) ? atoi(v) : 0;
+  return b > 0 ? b : 8;
+}
+
 int launch_plan(const fbg_plan& p, const fbg::GemmArgs& args, void* ws, int64_t M, int64_t N) {
   hipError_t e = hipSuccess;
   switch (p.variant) {
     case FBG_VARIANT_GENERIC:
-      e = fbg::launch_generic(args, p.config, p.grid, 8);
+      e = fbg::launch_generic(args, p.config, p.grid, raster_band());
       break;
     case FBG_VARIANT_SHORT_K256:
       e = fbg::launch_short_k256(args, p.config, p.grid);

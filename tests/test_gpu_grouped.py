@@ -216,3 +216,42 @@ def test_side_stream_and_unaligned_output(gpu):
     Cv = big[1:1 + 16 * 130].view(16, 130)          # 2-byte aligned only
     C = run(dd, "bf16", C=Cv)
     assert_within_tolerance(C, ref, "bf16", "unaligned C")
+
+
+def test_quantised_operands_feed_the_grouped_gemm(gpu):
+    """End to end on the GPU: bf16 activations and per-expert bf16 weights
+    quantised by the library's kernels, then the grouped GEMM; the codes and
+    scales equal the oracle's bit for bit, so the GEMM equals the grouped
+    GEMM on the oracle-quantised operands bit for bit, and the oracle's
+    grouped GEMM on them within tolerance."""
+    counts = [5, 0, 33, 2, 70]
+    E, N, K = len(counts), 260, 1024
+    off = np.concatenate([[0], np.cumsum(counts)])
+    M = int(off[-1])
+    rng = np.random.default_rng(77)
+    to_bits = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+    xb = to_bits(rng.normal(size=(M, K)))
+    wb = to_bits(rng.normal(size=(E, N, K)) * 0.02)
+    x = torch.from_numpy(xb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    w = torch.from_numpy(wb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    A, a_s = fbg.quantize_rows(x)
+    Bq = torch.empty((E, N, K), dtype=torch.float8_e4m3fn, device=DEV)
+    b_s = torch.empty((E, (N + 127) // 128, K // 128), dtype=torch.float32, device=DEV)
+    for e in range(E):
+        fbg.quantize_blocks(w[e], Bq[e], b_s[e])
+    offsets = torch.from_numpy(off.astype(np.int32)).to(DEV)
+    C = fbg.grouped_gemm(A, a_s, Bq, b_s, offsets)
+    torch.cuda.synchronize()
+    qa, sa = oracle.quantize_rows(xb)
+    qb = np.empty((E, N, K), np.uint8)
+    sb = np.empty((E, (N + 127) // 128, K // 128), np.float32)
+    for e in range(E):
+        qb[e], sb[e] = oracle.quantize_blocks(wb[e])
+    assert np.array_equal(A.view(torch.uint8).cpu().numpy(), qa)
+    assert np.array_equal(Bq.view(torch.uint8).cpu().numpy(), qb)
+    dd = to_dev({"A": qa, "a_s": sa, "B": qb, "b_s": sb, "offsets": off})
+    C2 = fbg.grouped_gemm(dd["A"], dd["a_s"], dd["B"], dd["b_s"], dd["offsets"])
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16))
+    assert_within_tolerance(C, oracle.grouped_gemm(qa, sa, qb, sb, off), "bf16", "quantised grouped")
