@@ -19,6 +19,8 @@ CPU oracle timed on a bounded sample of the same workload.
 
 Other modes (for profiles):
   --sweep FILE        every workload and sweep point, one JSON line each, to FILE
+  --dispatch-sweep FILE   the dispatcher's choice against every forced alternative
+                      on the pages' (M, N, K) shape sets, one JSON line per shape
   --copy-bytes B      only a plain device copy of B bytes (calibrates HBM counters)
   --op quantize       time the per-token 1x128 activation quantiser (bf16 -> E4M3
                       codes + fp32 scales) on the workload's A shape instead
@@ -343,6 +345,81 @@ def cpu_baseline(d, flops_per_call, budget_s=12.0):
             "sample": f"full workload GEMM (fp64 oracle, E4M3 decode) repeated {reps}x in {el:.1f} s"}
 
 
+def dispatch_sweep(path, torch, fbg, steps=100, warmup=10):
+    """Dispatcher evidence: on every (M, N, K) of the pages' shape sets
+    (N in {512, 1536, 4096, 8192}, K in {256, 1024, 4096}, M from 1 to 4096),
+    times the dispatcher's own choice and every forced alternative (each
+    generic tile, the main swap-AB tiles with and without split-K, the short-K
+    tiles at K = 256) the same way as the benchmark (HIP-graph replays over
+    input copies rotated past the MALL), one JSON line per shape with the
+    regret of the dispatcher's choice against the fastest alternative.  The
+    operands are random non-NaN E4M3 bytes and random scales made on the GPU
+    (timing only, no parity)."""
+    dev = torch.device("cuda:0")
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+
+    def codes(rows, cols):
+        c = torch.randint(0, 254, (rows, cols), device=dev, generator=gen, dtype=torch.int32)
+        return (c + (c >= 0x7F).int()).to(torch.uint8).view(torch.float8_e4m3fn)
+
+    with open(path, "w") as f:
+        for N in (512, 1536, 4096, 8192):
+            for K in (256, 1024, 4096):
+                for M in (1, 16, 32, 64, 128, 256, 512, 1024, 4096):
+                    G, NB = K // 128, (N + 127) // 128
+                    per_copy = M * K + N * K + 4 * M * G + 4 * NB * G + 2 * M * N
+                    copies = max(1, min(256, -(-2 * MALL_BYTES // per_copy)))
+                    base = {"A": codes(M, K), "B": codes(N, K),
+                            "a_s": torch.rand((M, G), device=dev, generator=gen) * 0.01 + 1e-3,
+                            "b_s": torch.rand((NB, G), device=dev, generator=gen) * 0.01 + 1e-3}
+                    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+                    outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+                    cands = [("auto", None)] + [("generic", c) for c in range(7)]
+                    cands += [(v, c) for v in ("swap_ab", "swap_ab_splitk") for c in (2, 4, 7, 12, 19)]
+                    if K == 256:
+                        cands += [("short_k256", c) for c in range(16)]
+                    cands += [("auto", None)]   # timed first and last: the faster of the two counts
+                    res = {}
+                    for variant, cfg in cands:
+                        p = fbg.plan(M, N, K, torch.bfloat16, cu, variant, 0) if cfg is None else None
+                        if cfg is not None:
+                            os.environ["FBG_FORCE_CONFIG"] = str(cfg)
+                        ws = torch.zeros(max(fbg.workspace_size(M, N, K, variant, 0), 16), dtype=torch.uint8,
+                                         device=dev)
+                        stream = torch.cuda.Stream()
+
+                        def step(i):
+                            t = sets[i % copies]
+                            fbg.gemm(t["A"], t["a_s"], t["B"], t["b_s"], out=outs[i % copies], workspace=ws,
+                                     stream=stream, variant=variant)
+
+                        try:
+                            ms, _ = time_steps(step, copies, steps, warmup, True, stream, torch)
+                            t_us = ms / steps * 1e3
+                            res[(variant, cfg)] = min(t_us, res.get((variant, cfg), t_us))
+                        except fbg.FP8BGError:
+                            pass
+                        finally:
+                            os.environ.pop("FBG_FORCE_CONFIG", None)
+                        if cfg is None:
+                            auto_plan = p
+                    auto_us = res[("auto", None)]
+                    best = min((v for v in res.items() if v[0][0] != "auto"), key=lambda kv: kv[1])
+                    line = {"M": M, "N": N, "K": K, "auto": {"variant": auto_plan["variant_name"],
+                                                              "cfg": auto_plan["config"],
+                                                              "split_k": auto_plan["split_k"],
+                                                              "us": round(auto_us, 3)},
+                            "best": {"variant": best[0][0], "cfg": best[0][1], "us": round(best[1], 3)},
+                            "regret": round(auto_us / best[1] - 1.0, 4),
+                            "all": {f"{v}:{c}": round(t, 3) for (v, c), t in res.items()}}
+                    f.write(json.dumps(line) + "\n")
+                    f.flush()
+                    print(json.dumps({k: line[k] for k in ("M", "N", "K", "auto", "best", "regret")}), flush=True)
+                    del sets, outs, base
+
+
 def copy_only(nbytes, torch, reps=5):
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
     dst = torch.empty_like(src)
@@ -365,6 +442,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep", default=None)
+    ap.add_argument("--dispatch-sweep", default=None,
+                    help="time the dispatcher's choice against every forced alternative on the pages' shape sets")
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--variant", default="auto", help="force a kernel variant (tuning)")
     ap.add_argument("--split", type=int, default=0, help="force a split-K count (tuning)")
@@ -391,6 +470,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
 
+    if args.dispatch_sweep:
+        dispatch_sweep(args.dispatch_sweep, torch, fbg)
+        return
     if args.sweep:
         with open(args.sweep, "w") as f:
             for name, w in W.WORKLOADS.items():

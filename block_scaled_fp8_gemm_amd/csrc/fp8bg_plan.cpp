@@ -26,60 +26,53 @@ int64_t skinny_tiles(const SkinnyCfg& c, int64_t M, int64_t N) {
   return cdiv(N, skinny_tile_n(c)) * cdiv(M, skinny_tile_m(c));
 }
 
-// Tile configurations, from on-device configuration sweeps of every
-// workload shape and sweep point (bench.py with forced variant, split and
-// configuration; the results are kept in profiles/).  The small shapes are
-// bound by how many bytes each compute unit must pull (each CU sustains
-// ~25-28 GB/s at these sizes) plus the split-K handshake, so the rules
-// pick the tile that fills the device with the fewest bytes per CU.
+// Tile configurations and variant choice, from on-device sweeps (bench.py
+// --sweep over the workloads, and --dispatch-sweep: every forced alternative
+// on 108 shapes of the pages' sets N in {512, 1536, 4096, 8192}, K in {256,
+// 1024, 4096}, M = 1 .. 4096).  What those sweeps show: each compute unit
+// pulls its tiles' rows at a roughly fixed rate, so a launch costs about its
+// busiest CU's rows x K; the split-K handshake (three memory round trips)
+// costs ~1.5-2 us, more than splitting saves unless K is long and the
+// unsplit grid fills at most half the device.
 //
-// Swap-AB: 32 n x 64 m tiles (config 4) read every weight row once for
-// M <= 64 and are used when they alone give every CU a workgroup (M > 16);
-// otherwise 32 n x 16 m tiles (config 7), split over K below until the
-// grid covers the device.
-int swap_cfg_for(int64_t M, int64_t N, int cu) {
-  if (M > 16 && cdiv(N, 32) * cdiv(M, 64) >= (int64_t)cu) return 4;
-  return 7;
-}
+// Swap-AB (small M): the smallest tile whose grid still fits the device in
+// one wave of workgroups -- 16 n x 16 m (config 2), else 32 n x 16 m
+// (config 7), else, for long K and M <= 64, 32 n x 64 m (config 19); none
+// fits -> the generic kernel.  Split over K only for K >= 2048, M > 1 and a
+// grid of at most half the device.  (K = 1024, N = 512, M = 1: 2.85 us
+// unsplit 16x16 against 4.59 us for 32x16 split in two.)
+struct SwapPick {
+  int cfg;
+  int64_t S;
+};
 
-// Short-K (two groups, one per wave): 16 n x 16 m up to M = 48 (config 12),
-// 32 n x 32 m up to M = 200 (config 15), 32 n x 64 m up to M = 256
-// (config 10); above, 32 n x 32 m with one wave taking both groups
-// (config 6).
-int short_cfg_for(int64_t M) {
-  if (M <= 48) return 12;
-  if (M <= 200) return 15;
-  if (M <= 256) return 10;
-  return 6;
-}
-
-// Generic: each compute unit pulls its tiles' A and B rows at a roughly
-// fixed rate (~25 GB/s per CU on this GPU, whatever the tile), so a launch
-// costs about (workgroups per CU) x (BM + BN) x K bytes per CU.  The planner
-// takes the configuration with the fewest such bytes; on a tie, the larger
-// tile (more MFMA work per LDS byte, fewer workgroups), then more waves.  For large M this is
-// the 256 x 256 tile; in the mid-M band it picks the small tiles that put a
-// workgroup on every CU (measured: M = 128, N = 8192, K = 1024 runs in
-// 6.8 us with 64 x 64 tiles against 9.3 us with 64 x 128).
-int64_t generic_cost(const GenericCfg& g, int64_t M, int64_t N, int cu) {
-  const int64_t wgs = cdiv(M, g.bm) * cdiv(N, g.bn);
-  return cdiv(wgs, cu) * (g.bm + g.bn);
-}
-
-int generic_cfg_for(int64_t M, int64_t N, int cu) {
-  int best = 0;
-  for (int c = 1; c < kNumGenericCfgs; ++c) {
-    const GenericCfg& g = kGenericCfgs[c];
-    const GenericCfg& b = kGenericCfgs[best];
-    const int64_t cg = generic_cost(g, M, N, cu), cb = generic_cost(b, M, N, cu);
-    const int wg = g.waves_m * g.waves_n, wb = b.waves_m * b.waves_n;
-    if (cg < cb || (cg == cb && (g.bm * g.bn > b.bm * b.bn || (g.bm * g.bn == b.bm * b.bn && wg > wb)))) best = c;
+bool swap_pick(int64_t M, int64_t N, int64_t G, int cu, SwapPick* out) {
+  const int64_t W2 = cdiv(N, 16) * cdiv(M, 16), W7 = cdiv(N, 32) * cdiv(M, 16), W19 = cdiv(N, 32) * cdiv(M, 64);
+  int64_t W;
+  if (W2 <= cu) {
+    out->cfg = 2;
+    W = W2;
+  } else if (W7 <= cu) {
+    out->cfg = 7;
+    W = W7;
+  } else if (G >= 16 && M <= 64 && W19 <= cu) {
+    out->cfg = 19;
+    W = W19;
+  } else {
+    return false;
   }
-  return best;
+  out->S = 1;
+  if (G >= 16 && M > 1 && 2 * W <= cu) {
+    const int64_t cap = G / kSwapCfgs[out->cfg].kw;
+    const int64_t want = cdiv(cu, W);
+    out->S = want < cap ? want : cap;
+    if (out->S < 1) out->S = 1;
+  }
+  return true;
 }
 
-// Split K until the grid covers the device once, keeping at least one group
-// per wave in every split.
+// Forced split-K without a split count: split until the grid covers the
+// device once, keeping at least one group per wave in every split.
 int64_t swap_split(const SkinnyCfg& k, int64_t tiles, int64_t G, int cu) {
   const int64_t want = cdiv(cu, tiles);
   const int64_t cap = G / k.kw > 1 ? G / k.kw : 1;
@@ -87,17 +80,64 @@ int64_t swap_split(const SkinnyCfg& k, int64_t tiles, int64_t G, int cu) {
   return S < 1 ? 1 : S;
 }
 
-// The swap-AB kernels' cost in the units of generic_cost x groups: per-CU
-// rows x groups, weighted 3/2 because their direct-to-register loads were
-// measured ~1.4x slower per byte than the generic kernel's LDS DMA, plus
-// the split-K handshake (~1.3 us, about 32 rows x 8 groups at the measured
-// rate) when K is split.
-int64_t swap_cost(int64_t M, int64_t N, int64_t G, int cu) {
-  const SkinnyCfg& k = kSwapCfgs[swap_cfg_for(M, N, cu)];
-  const int64_t tiles = skinny_tiles(k, M, N);
-  const int64_t S = swap_split(k, tiles, G, cu);
-  const int64_t rows = skinny_tile_m(k) + skinny_tile_n(k);
-  return cdiv(tiles * S, cu) * rows * cdiv(G, S) * 3 / 2 + (S > 1 ? 256 : 0);
+// The swap-AB tile when a variant is forced without a configuration and
+// swap_pick finds none: 32 n x 64 m tiles (config 4) when they alone give
+// every CU a workgroup, else 32 n x 16 m (config 7).
+int swap_cfg_for(int64_t M, int64_t N, int64_t G, int cu) {
+  SwapPick p;
+  if (swap_pick(M, N, G, cu, &p)) return p.cfg;
+  if (M > 16 && cdiv(N, 32) * cdiv(M, 64) >= (int64_t)cu) return 4;
+  return 7;
+}
+
+// Short-K (K == 256, two groups): 16 n x 16 m tiles with one group per wave
+// (config 12) while their grid fits two workgroups per CU; the automatic
+// dispatch sends larger shapes to the generic kernel (K = 256, N = 8192,
+// M = 512: 8.6 us against 13.0 us), and a forced short-K launch of such a
+// shape takes 32 n x 32 m (config 15) up to M = 200, 32 n x 64 m
+// (config 10) up to M = 256, else 32 n x 32 m with one wave taking both
+// groups (config 6).
+bool short_fits(int64_t M, int64_t N, int cu) { return cdiv(N, 16) * cdiv(M, 16) <= 2 * (int64_t)cu; }
+
+int short_cfg_for(int64_t M, int64_t N, int cu) {
+  if (short_fits(M, N, cu) || M <= 48) return 12;
+  if (M <= 200) return 15;
+  if (M <= 256) return 10;
+  return 6;
+}
+
+// Generic: a launch costs about (workgroups per CU) x (BM + BN) x K bytes
+// per CU, so the planner takes the configuration with the fewest such bytes;
+// on a tie, the larger tile (more MFMA work per LDS byte, fewer workgroups),
+// then, for K >= 2048, the deeper LDS ring (64 x 128 with 4 stages over
+// 128 x 64 with 3: K = 4096, N = 4096, M = 512 in 25.0 us against 26.9 us),
+// else more waves.  For large M this is the 256 x 256 tile; in the mid-M
+// band it picks the small tiles that put a workgroup on every CU (measured:
+// M = 128, N = 8192, K = 1024 runs in 6.8 us with 64 x 64 tiles against
+// 9.3 us with 64 x 128).
+int64_t generic_cost(const GenericCfg& g, int64_t M, int64_t N, int cu) {
+  const int64_t wgs = cdiv(M, g.bm) * cdiv(N, g.bn);
+  return cdiv(wgs, cu) * (g.bm + g.bn);
+}
+
+int generic_cfg_for(int64_t M, int64_t N, int64_t G, int cu) {
+  int best = 0;
+  for (int c = 1; c < kNumGenericCfgs; ++c) {
+    const GenericCfg& g = kGenericCfgs[c];
+    const GenericCfg& b = kGenericCfgs[best];
+    const int64_t cg = generic_cost(g, M, N, cu), cb = generic_cost(b, M, N, cu);
+    bool better = cg < cb;
+    if (cg == cb) {
+      if (g.bm * g.bn != b.bm * b.bn)
+        better = g.bm * g.bn > b.bm * b.bn;
+      else if (G >= 16 && g.stages != b.stages)
+        better = g.stages > b.stages;
+      else
+        better = g.waves_m * g.waves_n > b.waves_m * b.waves_n;
+    }
+    if (better) best = c;
+  }
+  return best;
 }
 
 }  // namespace
@@ -129,18 +169,16 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
   }
 
   int v = variant;
+  SwapPick pick{7, 1};
+  const bool picked = swap_pick(M, N, G, cu, &pick);
   if (v == FBG_VARIANT_AUTO) {
-    // Swap-AB (maybe split over K) for M <= 16; the generic kernel above
-    // M = 128; in between, whichever pulls fewer bytes per CU by the cost
-    // model of generic_cost / swap_cost.
+    // K == 256: short-K while its 16x16 grid fits, else generic.  Otherwise
+    // swap-AB for M <= 16 and, up to M = 256, when swap_pick finds a tile;
+    // the generic kernel for the rest.
     if (K == 256 && M <= 1024)
-      v = FBG_VARIANT_SHORT_K256;
-    else if (M <= 16)
+      v = short_fits(M, N, cu) ? FBG_VARIANT_SHORT_K256 : FBG_VARIANT_GENERIC;
+    else if (M <= 16 || (M <= 256 && picked))
       v = FBG_VARIANT_SWAP_AB;
-    else if (M <= 128)
-      v = generic_cost(kGenericCfgs[generic_cfg_for(M, N, cu)], M, N, cu) * G <= swap_cost(M, N, G, cu)
-              ? FBG_VARIANT_GENERIC
-              : FBG_VARIANT_SWAP_AB;
     else
       v = FBG_VARIANT_GENERIC;
   }
@@ -152,7 +190,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
     if (force_cfg >= n) return FBG_ERROR_UNSUPPORTED;
   }
   if (v == FBG_VARIANT_GENERIC) {
-    const int c = force_cfg >= 0 ? force_cfg : generic_cfg_for(M, N, cu);
+    const int c = force_cfg >= 0 ? force_cfg : generic_cfg_for(M, N, G, cu);
     const GenericCfg& g = kGenericCfgs[c];
     out->config = c;
     out->tile_m = g.bm;
@@ -160,7 +198,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
     out->waves = g.waves_m * g.waves_n;
     out->grid = cdiv(M, g.bm) * cdiv(N, g.bn);
   } else if (v == FBG_VARIANT_SHORT_K256) {
-    const int c = force_cfg >= 0 ? force_cfg : short_cfg_for(M);
+    const int c = force_cfg >= 0 ? force_cfg : short_cfg_for(M, N, cu);
     const SkinnyCfg& k = kShortCfgs[c];
     out->config = c;
     out->tile_m = skinny_tile_m(k);
@@ -168,14 +206,17 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
     out->waves = k.kw;
     out->grid = skinny_tiles(k, M, N);
   } else {  // SWAP_AB or SWAP_AB_SPLITK
-    const int c = force_cfg >= 0 ? force_cfg : swap_cfg_for(M, N, cu);
+    const int c = force_cfg >= 0 ? force_cfg : (picked ? pick.cfg : swap_cfg_for(M, N, G, cu));
     const SkinnyCfg& k = kSwapCfgs[c];
     const int64_t tiles = skinny_tiles(k, M, N);
     int64_t S = 1;
     if (split_k > 0) {
       S = split_k;
-    } else if (variant == FBG_VARIANT_AUTO || variant == FBG_VARIANT_SWAP_AB_SPLITK) {
-      S = swap_split(k, tiles, G, cu);
+    } else if (variant == FBG_VARIANT_AUTO) {
+      // The picked split (or none) when the picked tile is used.
+      S = (picked && c == pick.cfg) ? pick.S : 1;
+    } else if (variant == FBG_VARIANT_SWAP_AB_SPLITK) {
+      S = swap_split(k, tiles, G, cu);  // forced split-K: fill the device
     }
     if (variant == FBG_VARIANT_AUTO) v = S > 1 ? FBG_VARIANT_SWAP_AB_SPLITK : FBG_VARIANT_SWAP_AB;
     out->variant = v;
