@@ -328,21 +328,41 @@ def cpu_baseline_quantize(bits, budget_s=12.0, weights=False):
             "kind": "oracle", "sample": f"full {'weight' if weights else 'activation'} matrix quantised {reps}x in {el:.1f} s"}
 
 
-def cpu_baseline(d, flops_per_call, budget_s=12.0):
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(d, flops_per_call, budget_s=12.0, single_budget_s=4.0):
     """The oracle as it stands, on the host's cores, repeated over the full
-    workload until about `budget_s` of CPU time has passed."""
+    workload until about `budget_s` of CPU time has passed; then once more on
+    one thread for about `single_budget_s`."""
     import oracle
     oracle.block_gemm(d["A"][:1], d["a_s"][:1], d["B"], d["b_s"])  # load the library
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.block_gemm(d["A"], d["a_s"], d["B"], d["b_s"])
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 1000:
-            break
-    return {"value": round(reps * flops_per_call / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+
+    def timed(budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.block_gemm(d["A"], d["a_s"], d["B"], d["b_s"])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or reps >= 20000:
+                return reps, el
+
+    cores = oracle.threads()
+    reps, el = timed(budget_s)
+    oracle.set_threads(1)
+    reps1, el1 = timed(single_budget_s)
+    oracle.set_threads(cores)
+    return {"value": round(reps * flops_per_call / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"full workload GEMM (fp64 oracle, E4M3 decode) repeated {reps}x in {el:.1f} s"}
+            "sample": f"full workload GEMM (fp64 oracle, E4M3 decode) repeated {reps}x in {el:.1f} s",
+            "value_1_thread": round(reps1 * flops_per_call / el1 / 1e12, 6), "cpu": host_cpu_model()}
 
 
 def dispatch_sweep(path, torch, fbg, steps=100, warmup=10):
@@ -420,6 +440,23 @@ def dispatch_sweep(path, torch, fbg, steps=100, warmup=10):
                     del sets, outs, base
 
 
+def copy_floor_us(nbytes, torch, steps=200, warmup=20):
+    """The same-bytes floor of a launch on this GPU: a device-to-device copy
+    that reads nbytes/2 and writes nbytes/2, timed like the kernels (HIP-graph
+    replays, buffers rotated past the MALL).  Returns microseconds per copy."""
+    half = max(16, (nbytes // 2 + 15) // 16 * 16)
+    copies = max(2, min(256, -(-2 * MALL_BYTES // (2 * half))))
+    src = [torch.empty(half, dtype=torch.uint8, device="cuda:0").fill_(1) for _ in range(copies)]
+    dst = [torch.empty(half, dtype=torch.uint8, device="cuda:0") for _ in range(copies)]
+    stream = torch.cuda.Stream()
+
+    def step(i):
+        dst[i % copies].copy_(src[i % copies], non_blocking=True)
+
+    ms, _ = time_steps(step, copies, steps, warmup, True, stream, torch)
+    return ms / steps * 1e3
+
+
 def copy_only(nbytes, torch, reps=5):
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
     dst = torch.empty_like(src)
@@ -484,7 +521,8 @@ def main():
                                 "variant": r["plan"]["variant_name"], "cfg": r["plan"]["config"],
                                 "split_k": r["plan"]["split_k"], "grid": r["plan"]["grid"],
                                 "us": round(r["ms_per_step"] * 1e3, 3), "tflops": round(r["tflops"], 2),
-                                "gbs": round(r["gbs"], 1), "roofline": r["roof"], "copies": r["copies"]}
+                                "gbs": round(r["gbs"], 1), "roofline": r["roof"], "copies": r["copies"],
+                                "copy_floor_us": round(copy_floor_us(r["alg_bytes"], torch), 3)}
                         f.write(json.dumps(line) + "\n")
                         f.flush()
                         print(json.dumps(line), flush=True)
@@ -578,6 +616,9 @@ def main():
                    "input_copies": r["copies"], "graphs": not args.no_graph},
         "roofline": roof,
     }
+    fl = copy_floor_us(r["alg_bytes"], torch)
+    line["copy_floor"] = {"us": round(fl, 3), "bytes": r["alg_bytes"],
+                          "frac_of_floor": round(fl / (r["ms_per_step"] * 1e3), 4)}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r["d"], 2 * M * w.N * w.K)
     print(json.dumps(line), flush=True)

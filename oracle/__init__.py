@@ -59,6 +59,8 @@ def _load():
                                                  ctypes.c_void_p, ctypes.c_void_p]
     lib.fp8bg_oracle_threads.restype = ctypes.c_int
     lib.fp8bg_oracle_threads.argtypes = []
+    lib.fp8bg_oracle_set_threads.restype = None
+    lib.fp8bg_oracle_set_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -156,6 +158,12 @@ def bits_to_f64(bits, out_dtype) -> np.ndarray:
 def threads() -> int:
     """Threads the oracle's OpenMP loop uses."""
     return int(_load().fp8bg_oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Sets the oracle's OpenMP thread count (for timing only; results do not
+    depend on it: every output element is computed by one thread)."""
+    _load().fp8bg_oracle_set_threads(int(n))
 
 
 # (precision p incl. hidden bit, minimum normal exponent) per output dtype

@@ -309,3 +309,15 @@ int fp8bg_oracle_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the thread count of the OpenMP loops (timing of the oracle on one
+ * core and on all of them); no effect on any result. */
+void fp8bg_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
