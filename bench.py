@@ -562,6 +562,9 @@ def main():
                        "graphs": not args.no_graph},
             "roofline": dict(r["roof"], traffic=None),
         }
+        fl = copy_floor_us(r["alg_bytes"], torch)
+        line["copy_floor"] = {"us": round(fl, 3), "bytes": r["alg_bytes"],
+                              "frac_of_floor": round(fl / (r["ms_per_step"] * 1e3), 4)}
         rec = traffic_record(mw.name)
         if (rec is not None and args.cfg is None and rec.get("source_hash") == kernel_source_hash()
                 and rec.get("variant") == "grouped" and rec.get("config") == r["cfg"] and rec.get("out") == out):
