@@ -28,6 +28,14 @@
  * the MFMA units, then folds it as acc = fma(P, a_s*b_s, acc) in group order;
  * the cast to the output dtype is round-to-nearest-even.  Every call is
  * deterministic: the same inputs give the same bits on every run and stream.
+ *
+ * Environment variables (tuning and test hooks, read on every call; unset in
+ * normal use): FBG_FORCE_CONFIG=<i> pins the tile configuration index of the
+ * chosen variant (for fp8_block_gemm_grouped, the grouped configuration
+ * index); an index that does not exist -> UNSUPPORTED.  FBG_RASTER_BAND=<rows>
+ * sets the generic kernel's raster band height (default 8).  FBG_LOG=1
+ * prints each call's plan to stderr.  FBG_TEST_FAIL_ALLOC=1 makes the
+ * library-owned split-K workspace allocation fail (OUT_OF_MEMORY), for tests.
  */
 #ifndef FP8BG_H
 #define FP8BG_H
