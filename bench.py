@@ -49,11 +49,17 @@ KERNEL_SOURCES = ["block_scaled_fp8_gemm_amd/csrc/fp8bg_kernels.hip", "block_sca
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code (comments and whitespace removed, so a
+    comment edit does not invalidate a committed traffic profile)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -77,6 +77,12 @@ __device__ __forceinline__ void find_expert_tile(const int* offsets, int E, int 
 //
 // Each MFMA writes a fresh FP32 partial; its fold acc = fma(P, s, acc) is
 // issued after the next MFMA, in that MFMA's shadow.
+//
+// GRP = 1 is the grouped (mixture-of-experts) form: the grid enumerates
+// (row tile, column tile) with the row tiles of all experts in expert order,
+// each workgroup finds its expert with find_expert_tile, offsets B and b_s to
+// that expert's weight, and clamps its rows to the expert's range instead of
+// to M.  Everything after the tile's placement is shared with the dense form.
 // ===========================================================================
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int OUT, int GRP>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
