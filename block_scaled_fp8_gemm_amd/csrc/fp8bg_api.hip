@@ -150,6 +150,7 @@ extern "C" int fp8_block_gemm_ex(const void* A, const float* a_s, const void* B,
   args.K = (int)K;
   args.out = out_dtype;
   args.vec = (N % 4 == 0) && aligned(C, (uintptr_t)(4 * elem_size(out_dtype)));
+  if (args.vec && (N * elem_size(out_dtype)) % 16 == 0 && aligned(C, 16)) args.vec |= 2;  // 16-byte rows
   args.stream = stream;
 
   if (env_flag("FBG_LOG"))
@@ -279,6 +280,7 @@ extern "C" int fp8_block_gemm_grouped(const void* A, const float* a_s, const voi
   args.K = (int)K;
   args.out = out_dtype;
   args.vec = (N % 4 == 0) && aligned(C, (uintptr_t)(4 * elem_size(out_dtype)));
+  if (args.vec && (N * elem_size(out_dtype)) % 16 == 0 && aligned(C, 16)) args.vec |= 2;  // 16-byte rows
   args.stream = stream;
   if (env_flag("FBG_LOG"))
     fprintf(stderr, "fp8bg grouped: E=%lld M=%lld N=%lld K=%lld out=%d -> cfg=%d grid=%lld\n", (long long)E,

@@ -41,7 +41,8 @@ struct GemmArgs {
   void* C;
   int M, N, K;
   int out;
-  int vec;  // N % 4 == 0 and C aligned for 4-element vector stores
+  int vec;  // bit 0: N % 4 == 0 and C aligned for 4-element vector stores;
+            // bit 1: C rows 16-byte aligned (row pitch and base)
   hipStream_t stream;
 };
 

@@ -297,6 +297,61 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   // n = 16*j + 4*(lane >> 4) + r, r = 0..3, of the wave's sub-tile.
   const int m_l = m0 + wm * WM + (lane & 15);
   const int n_l = n0 + wn * WN + 4 * (lane >> 4);
+  if ((vec_ok & 2) && n0 + BN <= N) {
+    // Whole-row stores through LDS (every column of the tile in range, C rows
+    // 16-byte aligned): each wave writes its 16 x WN slab of converted
+    // outputs per 16-row block to LDS, then stores the slabs back 16
+    // contiguous bytes per lane, so one store instruction writes whole
+    // 64-128-byte row segments instead of 16 rows x 8 bytes.  As many row
+    // blocks as the LDS ring holds go in one phase (all of them for bf16 and
+    // fp16 tiles), with one barrier between a phase's writes and its reads.
+    // Slab rows are padded by 16 bytes: with an unpadded 128-byte pitch the 16
+    // rows a write instruction touches would all start in the same LDS bank.
+    typedef typename Out<OUT>::T T;
+    constexpr int ES = (int)sizeof(T), ROWB = WN * ES, ROWP = ROWB + 16, SLAB = 16 * ROWP;
+    constexpr int CHUNKS = 16 * ROWB / 16, PER_LANE = (CHUNKS + 63) / 64;
+    constexpr int FIT = (STAGES * STAGE_BYTES) / (NW * SLAB);
+    constexpr int PB = FIT < IB ? FIT : IB;  // row blocks per phase
+    static_assert(PB >= 1, "one row block of slabs must fit in the LDS ring");
+#pragma unroll
+    for (int i0 = 0; i0 < IB; i0 += PB) {
+      __syncthreads();  // the last group's (or the previous phase's) LDS reads are done
+#pragma unroll
+      for (int ii = 0; ii < PB; ++ii) {
+        if (i0 + ii >= IB) break;
+        uint8_t* slab = smem + (ii * NW + wave) * SLAB;
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+          T* d = reinterpret_cast<T*>(slab + (lane & 15) * ROWP) + 16 * j + 4 * (lane >> 4);
+          if constexpr (OUT == kOutFP32) {
+            *reinterpret_cast<v4f*>(d) = acc[i0 + ii][j];
+          } else {
+            typedef T T4 __attribute__((ext_vector_type(4)));
+            T4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = Out<OUT>::cvt(acc[i0 + ii][j][r]);
+            *reinterpret_cast<T4*>(d) = o;
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ii = 0; ii < PB; ++ii) {
+        if (i0 + ii >= IB) break;
+        const uint8_t* slab = smem + (ii * NW + wave) * SLAB;
+#pragma unroll
+        for (int t = 0; t < PER_LANE; ++t) {
+          const int q = t * 64 + lane;
+          const int row = q / (ROWB / 16), cb = (q % (ROWB / 16)) * 16;
+          const int m = m0 + wm * WM + 16 * (i0 + ii) + row;
+          if ((CHUNKS % 64 == 0 || q < CHUNKS) && m < m_end)
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(C) + ((int64_t)m * N + n0 + wn * WN) * ES + cb) =
+                *reinterpret_cast<const uint4*>(slab + row * ROWP + cb);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < IB; ++i)
 #pragma unroll

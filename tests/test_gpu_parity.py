@@ -297,3 +297,39 @@ def test_error_statuses(gpu):
     with pytest.raises(gpu.FP8BGError) as e:
         gpu.gemm(d["A"], d["a_s"], d["B"], d["b_s"], variant="swap_ab_splitk", split_k=4, workspace=ws)
     assert e.value.status == gpu.OUT_OF_MEMORY
+
+
+@pytest.mark.parametrize("variant,split", [("generic", 0), ("swap_ab", 0), ("swap_ab_splitk", 2), ("short_k256", 0)])
+def test_fp16_overflow_rounds_to_infinity(gpu, variant, split):
+    """fp16 output at its overflow threshold: exact sums 65519 (-> 65504),
+    65520 (the tie past the largest finite value -> +Inf), -65520 (-> -Inf)
+    and 2.57e7 (-> +Inf), bit for bit against the oracle's one-step rounding;
+    bf16 and fp32 of the same sums stay finite and exact."""
+    K = 256
+    codes = {v: int(workloads.e4m3_code_of_int(np.array([v]))[0]) for v in (1, 15, 16, 96, 448)}
+
+    def row(values):
+        r = np.zeros(K, dtype=np.uint8)
+        for k, v in enumerate(values):
+            r[k] = codes[abs(v)] | (0x80 if v < 0 else 0)
+        return r
+
+    B = np.stack([row([448] * 146 + [96, 15]),             # 65519
+                  row([448] * 146 + [96, 16]),             # 65520
+                  row([-448] * 146 + [-96, -16]),          # -65520
+                  row([448] * 128)])                       # 57344 per activation unit
+    A = np.zeros((3, K), dtype=np.uint8)
+    A[0] = codes[1]                                        # all ones
+    A[1] = codes[1]
+    A[2, :128] = codes[448]                                # 448 * 57344 * ... -> 2.57e7 on column 3
+    d = {"A": A, "a_s": np.ones((3, 2), np.float32), "B": B, "b_s": np.ones((1, 2), np.float32)}
+    ref = oracle.block_gemm(d["A"], d["a_s"], d["B"], d["b_s"])
+    assert ref[0, 0] == 65519 and ref[0, 1] == 65520 and ref[0, 2] == -65520 and ref[2, 3] == 448 * 448 * 128
+    dd = to_dev(d)
+    C = run(gpu, dd, "fp16", variant, split)
+    got = bits(C, "fp16")
+    want = oracle.round_bits(ref, "fp16")
+    assert got[0, 0] == 0x7BFF and got[0, 1] == 0x7C00 and got[0, 2] == 0xFC00 and got[2, 3] == 0x7C00
+    assert np.array_equal(got, want)
+    for out in ("bf16", "fp32"):
+        assert_bitwise(run(gpu, dd, out, variant, split), ref, out, f"{variant} {out}")
