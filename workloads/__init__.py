@@ -195,6 +195,8 @@ MOE_WORKLOADS = {
                                           note="256 tokens: 8 rows per expert on average"),
     "moe_t1024_e256_512x4096": MoEWorkload("moe_t1024_e256_512x4096", 1024, 256, 8, 512, 4096, seed=14,
                                            note="1024 tokens: 32 rows per expert on average"),
+    "moe_t2048_e256_512x4096": MoEWorkload("moe_t2048_e256_512x4096", 2048, 256, 8, 512, 4096, seed=16,
+                                           note="2048 tokens: 64 rows per expert on average"),
     "moe_t4096_e256_512x4096": MoEWorkload("moe_t4096_e256_512x4096", 4096, 256, 8, 512, 4096, seed=15,
                                            note="4096 tokens (prefill): 128 rows per expert on average"),
 }
