@@ -139,8 +139,13 @@ def gemm(A: torch.Tensor, a_s: torch.Tensor, B: torch.Tensor, b_s: torch.Tensor,
 
     A [M,K] and B [N,K]: float8_e4m3fn (or uint8 holding E4M3 codes);
     a_s [M, K/128], b_s [ceil(N/128), K/128]: float32; all contiguous on one
-    GPU.  variant/split_k force a kernel (see include/fp8bg.h); workspace is an
-    optional caller-owned byte buffer for split-K whose counter area is zero.
+    GPU.  variant/split_k force a kernel (see include/fp8bg.h).  workspace:
+    None (default) -- when the plan splits K, a zeroed byte tensor from
+    torch's caching allocator on the call's stream (cheap, and captured into
+    a HIP graph's memory pool like any tensor); "library" -- the C library's
+    own stream-ordered allocation (fp8_block_gemm), whose allocation and free
+    become graph nodes under capture; or a caller-owned byte tensor whose
+    counter area is zero.
     """
     lib = load()
     if A.dim() != 2 or B.dim() != 2:
@@ -159,6 +164,15 @@ def gemm(A: torch.Tensor, a_s: torch.Tensor, B: torch.Tensor, b_s: torch.Tensor,
         _check(out, "out", (out_dtype,), (M, N), dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     v, code = _variant_code(variant), _out_code(out_dtype)
+    if isinstance(workspace, str):
+        if workspace != "library":
+            raise ValueError('workspace must be None, "library" or a byte tensor')
+        workspace = None
+    elif workspace is None:
+        need = lib.fp8_block_gemm_workspace_size(M, N, K, v, split_k)
+        if 0 < need < ctypes.c_size_t(-1).value:   # an invalid request is reported by the call itself
+            with torch.cuda.stream(s):
+                workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     if v == 0 and split_k == 0 and workspace is None:
         st = lib.fp8_block_gemm(A.data_ptr(), a_s.data_ptr(), B.data_ptr(), b_s.data_ptr(), out.data_ptr(),
                                 M, N, K, code, s.cuda_stream)

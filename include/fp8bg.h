@@ -96,7 +96,11 @@ typedef struct fbg_plan {
  * (hipMallocAsync / hipFreeAsync), so concurrent calls on different streams
  * do not share it; failure -> OUT_OF_MEMORY before anything is launched.  Its
  * arrival counters are zeroed by a small kernel (no hipMemsetAsync), so the
- * call may be captured in a HIP graph as it is.
+ * call may be captured in a HIP graph as it is.  The stream-ordered
+ * allocation and free cost ~15-20 us per split-K call on this GPU, eager or
+ * captured (measured on 64x512x4096: 27 us eager, 22 us per graph replay,
+ * against 7 us and 6 us with a caller workspace): latency-sensitive callers
+ * pass their own workspace to fp8_block_gemm_ex.
  */
 int fp8_block_gemm(const void *A, const float *a_s, const void *B, const float *b_s,
                    void *C, int64_t M, int64_t N, int64_t K, int out_dtype, void *stream);

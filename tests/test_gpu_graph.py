@@ -125,6 +125,30 @@ def test_split_k_gemm_with_library_workspace_in_a_graph(gpu):
     C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
 
     def capture():
+        fbg.gemm(dd["A"], dd["a_s"], dd["B"], dd["b_s"], out=C, stream=torch.cuda.current_stream(),
+                 workspace="library")
+        return [C]
+
+    def eager():
+        return [fbg.gemm(dd["A"], dd["a_s"], dd["B"], dd["b_s"], workspace="library")]
+
+    def refill(i):
+        d = to_dev(workloads.make_inputs(M, N, K, seed=50 + i))
+        for k in dd:
+            dd[k].copy_(d[k])
+
+    replay_and_check(capture, eager, refill)
+
+
+def test_split_k_gemm_with_default_workspace_in_a_graph(gpu):
+    """The binding's default workspace (a zeroed torch tensor on the call's
+    stream) captured into the graph's memory pool."""
+    M, N, K = 16, 1536, 4096
+    assert fbg.plan(M, N, K)["split_k"] > 1
+    dd = to_dev(workloads.make_inputs(M, N, K, seed=33))
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+
+    def capture():
         fbg.gemm(dd["A"], dd["a_s"], dd["B"], dd["b_s"], out=C, stream=torch.cuda.current_stream())
         return [C]
 
@@ -132,7 +156,7 @@ def test_split_k_gemm_with_library_workspace_in_a_graph(gpu):
         return [fbg.gemm(dd["A"], dd["a_s"], dd["B"], dd["b_s"])]
 
     def refill(i):
-        d = to_dev(workloads.make_inputs(M, N, K, seed=50 + i))
+        d = to_dev(workloads.make_inputs(M, N, K, seed=60 + i))
         for k in dd:
             dd[k].copy_(d[k])
 

@@ -218,9 +218,34 @@ def test_concurrent_streams_with_library_workspace(gpu):
     outs = []
     for _ in range(4):
         with torch.cuda.stream(s1):
-            c1 = gpu.gemm(dd1["A"], dd1["a_s"], dd1["B"], dd1["b_s"], variant="swap_ab_splitk", split_k=8)
+            c1 = gpu.gemm(dd1["A"], dd1["a_s"], dd1["B"], dd1["b_s"], variant="swap_ab_splitk", split_k=8,
+                          workspace="library")
         with torch.cuda.stream(s2):
-            c2 = gpu.gemm(dd2["A"], dd2["a_s"], dd2["B"], dd2["b_s"], variant="swap_ab_splitk", split_k=4)
+            c2 = gpu.gemm(dd2["A"], dd2["a_s"], dd2["B"], dd2["b_s"], variant="swap_ab_splitk", split_k=4,
+                          workspace="library")
+        outs.append((c1, c2))
+    torch.cuda.synchronize()
+    for c1, c2 in outs:
+        assert_within_tolerance(c1, r1, "bf16")
+        assert_within_tolerance(c2, r2, "bf16")
+
+
+def test_concurrent_streams_with_default_workspace(gpu):
+    """The binding's default split-K workspace (a zeroed tensor from torch's
+    allocator on the call's stream) on two streams at once."""
+    d1 = workloads.make_inputs(64, 512, 4096, seed=23)
+    d2 = workloads.make_inputs(16, 1536, 4096, seed=24)
+    r1 = oracle.block_gemm(d1["A"], d1["a_s"], d1["B"], d1["b_s"])
+    r2 = oracle.block_gemm(d2["A"], d2["a_s"], d2["B"], d2["b_s"])
+    dd1, dd2 = to_dev(d1), to_dev(d2)
+    assert gpu.plan(64, 512, 4096)["split_k"] > 1 and gpu.plan(16, 1536, 4096)["split_k"] > 1
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            c1 = gpu.gemm(dd1["A"], dd1["a_s"], dd1["B"], dd1["b_s"])
+        with torch.cuda.stream(s2):
+            c2 = gpu.gemm(dd2["A"], dd2["a_s"], dd2["B"], dd2["b_s"])
         outs.append((c1, c2))
     torch.cuda.synchronize()
     for c1, c2 in outs:
