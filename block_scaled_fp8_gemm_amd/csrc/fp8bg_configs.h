@@ -7,15 +7,17 @@
 namespace fbg {
 
 // Generic LDS-staged kernel: id, block tile BM x BN, waves WAVES_M x WAVES_N,
-// LDS ring depth in groups.
-#define FBG_GENERIC_CFGS(X) \
-  X(0, 128, 128, 2, 2, 4)   \
-  X(1, 256, 128, 2, 2, 3)   \
-  X(2, 64, 128, 1, 2, 4)    \
-  X(3, 256, 256, 2, 4, 2)   \
-  X(4, 64, 64, 1, 2, 4)     \
-  X(5, 128, 64, 2, 2, 3)    \
-  X(6, 64, 32, 1, 2, 4)
+// LDS ring depth in groups, row-scale staging (1: chunks of several groups
+// per row, loaded a few rows' runs per instruction; 0: one load per row and
+// group, staged in the ring slot).
+#define FBG_GENERIC_CFGS(X)  \
+  X(0, 128, 128, 2, 2, 4, 0) \
+  X(1, 256, 128, 2, 2, 3, 0) \
+  X(2, 64, 128, 1, 2, 4, 0)  \
+  X(3, 256, 256, 2, 4, 2, 1) \
+  X(4, 64, 64, 1, 2, 4, 0)   \
+  X(5, 128, 64, 2, 2, 3, 0)  \
+  X(6, 64, 32, 1, 2, 4, 0)
 
 // Skinny kernels (swap-AB and its split-K form): id, NB16 16-row blocks of
 // weight rows (output columns n), MB16 16-column blocks of activation rows
@@ -78,9 +80,9 @@ namespace fbg {
   X(9, 4, 4, 4, 1)          \
   X(10, 8, 2, 2, 1)
 
-struct GenericCfg { int bm, bn, waves_m, waves_n, stages; };
+struct GenericCfg { int bm, bn, waves_m, waves_n, stages, scale_chunks; };
 constexpr GenericCfg kGenericCfgs[] = {
-#define X(id, bm, bn, wm, wn, st) {bm, bn, wm, wn, st},
+#define X(id, bm, bn, wm, wn, st, sch) {bm, bn, wm, wn, st, sch},
     FBG_GENERIC_CFGS(X)
 #undef X
 };

@@ -141,6 +141,11 @@ typedef __amdgpu_buffer_rsrc_t buf_rsrc;
 __device__ __forceinline__ buf_rsrc make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
 }
+// A resource of `bytes` bytes: loads at or past the end (voff, not soff,
+// counts) read zeros and touch no memory.
+__device__ __forceinline__ buf_rsrc make_rsrc_n(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 __device__ __forceinline__ void lds_dma16(buf_rsrc r, uint32_t voff, int soff, lds_u8* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voff, soff, 0, 0);
 }

@@ -60,8 +60,10 @@ __device__ __forceinline__ void find_expert_tile(const int* offsets, int E, int 
 //
 // Loads go straight from global memory into LDS (buffer_load_dwordx4 ... lds):
 // no staging registers and no LDS store instructions.  Every thread issues
-// the same LPG loads per group (A images, B images, one a_s and one b_s
-// load), so one vmcnt bound says "this wave's loads of group g have landed";
+// the same LPG loads per group (A images, B images, one a_s load -- the
+// group's row scales, or with SCH = 1 a part of a later chunk of them -- and
+// one b_s load), so one vmcnt bound says "this wave's loads of group g have
+// landed";
 // a barrier then makes the whole tile visible.  The one barrier per group
 // sits in the group's last row block, once every LDS read of the group has
 // been issued: past it, the slot is refilled with the group STAGES ahead,
@@ -72,11 +74,11 @@ __device__ __forceinline__ void find_expert_tile(const int* offsets, int E, int 
 // m on the second, so a lane ends with ONE output row m and 4 consecutive
 // columns n of each 16x16 block.  The block's scale a_s[m,g] * b_s[n/128,g]
 // is then one value per lane (a wave's columns share one b_s block), the
-// a_s of a lane's rows is one short LDS read per group, and the epilogue
+// a_s of a lane's rows are a few short LDS reads per group, and the epilogue
 // stores 4 outputs per lane at once.
 //
 // Each MFMA writes a fresh FP32 partial; its fold acc = fma(P, s, acc) is
-// issued after the next MFMA, in that MFMA's shadow.
+// issued two MFMAs later, in their shadow.
 //
 // GRP = 1 is the grouped (mixture-of-experts) form: the grid enumerates
 // (row tile, column tile) with the row tiles of all experts in expert order,
@@ -84,7 +86,7 @@ __device__ __forceinline__ void find_expert_tile(const int* offsets, int E, int 
 // that expert's weight, and clamps its rows to the expert's range instead of
 // to M.  Everything after the tile's placement is shared with the dense form.
 // ===========================================================================
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int OUT, int GRP>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SCH, int OUT, int GRP>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
     const uint8_t* __restrict__ A, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
     const float* __restrict__ b_s, void* __restrict__ C, int M, int N, int K, int band, int vec_ok,
@@ -95,16 +97,30 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   constexpr int IB = WM / 16, JB = WN / 16;
   constexpr int A_PER_T = BM * 8 / NT, B_PER_T = BN * 8 / NT;
   constexpr int LPG = A_PER_T + B_PER_T + 2;         // vector-memory loads per group per thread
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, S_BYTES = BM * 4 + 64 * 4;
-  constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
+  // A ring slot holds a group's A and B tiles, its b_s (64 floats) and, with
+  // SCH = 0, its row scales a_s (BM floats).
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, S_BYTES = 64 * 4 + (SCH ? 0 : BM * 4);
+  constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES, RING_BYTES = STAGES * STAGE_BYTES;
+  // With SCH = 1 the row scales travel in chunks of CH groups per row (CH * 4
+  // contiguous bytes of a_s), three chunk buffers deep, outside the ring.  A
+  // chunk is NQ load images of 256 bytes (one 4-byte load per lane each), 268
+  // bytes apart.  CH = 8 where the workgroups per CU that the LDS allows stay
+  // those of the SCH = 0 ring, else 4.
+  constexpr int QSTRIDE = 256 + 12;
+  constexpr int LDS_CU = 160 * 1024, PER_CU = LDS_CU / (STAGES * (A_BYTES + B_BYTES + 64 * 4 + BM * 4));
+  constexpr int CH = LDS_CU / (RING_BYTES + 3 * (BM * 8 / 64) * QSTRIDE) >= PER_CU ? 8 : 4;
+  constexpr int NQ = BM * CH / 64, CB_BYTES = SCH ? NQ * QSTRIDE : 0;
+  constexpr int NBI = 64 / (CH * IB);                // row classes per load image
+  constexpr int RF = 64 * NW / BM;                   // loads of each image per chunk
   static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile images must split evenly over waves");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one b_s block");
-  static_assert(BM >= 64 && BM % 64 == 0, "a_s rows are staged 64 per wave instruction");
-  static_assert(IB == 4 || IB == 8, "a lane reads its row scales as one or two 16-byte words");
-  static_assert(STAGES >= 2 && STAGES <= 4 && STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring must fit in 160 KB");
-  static_assert((STAGES - 1) * LPG < 64, "vmcnt counts at most 63 outstanding loads");
+  static_assert(BM % 64 == 0 && (RF == 1 || RF == 2) && CH % RF == 0, "a chunk's images must split evenly over the waves");
+  static_assert(CH * IB <= 64 && 64 % (CH * IB) == 0, "a load image holds whole row classes");
+  static_assert(SCH || IB == 4 || IB == 8, "a lane reads its row scales of a slot as one or two 16-byte words");
+  static_assert(STAGES >= 2 && STAGES <= 4 && LDS_CU / (RING_BYTES + 3 * CB_BYTES) >= PER_CU, "LDS ring must fit in 160 KB");
+  static_assert((STAGES - 1) * LPG + CH / RF < 64, "vmcnt counts at most 63 outstanding loads");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[STAGES * STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[RING_BYTES + 3 * CB_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -161,31 +177,67 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
     const int gr = (n0 + r) < N ? r : (N - 1 - n0);
     boff[i] = (uint32_t)gr * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ swz_row(r));
   }
-  // a_s of the tile's rows, staged transposed: slot (w*16 + r)*IB + i holds
-  // row w*WM + 16*i + r, so the IB row scales a lane needs (its row r = l & 15
-  // in each of its wave's row blocks) are contiguous.  Wave w stages slots
-  // (64w mod BM) + lane.
+  // Row scales, SCH = 1: chunk c (groups CH*c .. CH*c + CH-1 of every tile
+  // row) sits in chunk buffer c mod 3.  Row class b (b = wm*16 + r: the IB rows
+  // wm*WM + 16*i + r that lane r of the waves in wave row wm needs) is stored
+  // as [i][group]; image q holds classes q*NBI .. q*NBI + NBI-1.  An image
+  // load (lane l: class q*NBI + l / (CH*IB), row i = (l mod CH*IB) / CH,
+  // group l mod CH) reads CH consecutive groups of a row with CH adjacent
+  // lanes, so it touches 64/CH short runs of a_s where one load per row and
+  // group would touch 64 separate rows.  A lane reads its IB scales of a
+  // group CH floats apart; the 268-byte image pitch (67 words, 3 mod 64)
+  // keeps the 16 lanes of a read, and of a paired read of rows i and i+1, on
+  // different banks.  The group loop issues one image load per wave per
+  // group, the next chunk's images spread over the current chunk's CH groups
+  // (with RF = 2, two waves load each image).  Loads past the end of a_s read
+  // zeros (the resource's size is exact); the values of groups past G are
+  // never used.
+  const int ch_sub = lane / (CH * IB), ch_i = (lane % (CH * IB)) / CH, ch_grp = lane % CH;
+  auto as_off = [&](int q, int c) {  // a_s byte offset of this lane's element of image q of chunk c
+    const int b = q * NBI + ch_sub;
+    const int row = m0 + (b / 16) * WM + 16 * ch_i + (b % 16);
+    const int r = row < m_end ? row : (m_end - 1);
+    return (uint32_t)r * (uint32_t)G * 4u + 4u * (uint32_t)(c * CH + ch_grp);
+  };
+  // Row scales, SCH = 0: a_s of a group staged in its ring slot, transposed:
+  // slot (w*16 + r)*IB + i holds row w*WM + 16*i + r, so the IB row scales a
+  // lane needs (its row r = l & 15 in each of its wave's row blocks) are
+  // contiguous.  Wave w stages slots (64w mod BM) + lane: one load per row
+  // and group.
   const int slot = (wave * 64) % BM + lane;
   const int srow = (slot / (16 * IB)) * WM + 16 * (slot % IB) + (slot / IB) % 16;
   const int sr = (m0 + srow) < m_end ? (m0 + srow) : (m_end - 1);
   const uint32_t soff = (uint32_t)sr * (uint32_t)G * 4u;
-  // b_s of the tile's column blocks (lane l holds block n0/128 + l, clamped),
-  // so the loop issues no scalar-memory loads.
-  const int bblk = ((n0 >> 7) + lane) < nblk ? ((n0 >> 7) + lane) : (nblk - 1);
+  // b_s of the tile's column blocks (lane l holds block n0/128 + l, clamped to
+  // the tile's last block), so the loop issues no scalar-memory loads.
+  const int bl = lane < (BN + 127) / 128 ? lane : (BN + 127) / 128 - 1;
+  const int bblk = ((n0 >> 7) + bl) < nblk ? ((n0 >> 7) + bl) : (nblk - 1);
   const uint32_t bsoff = (uint32_t)bblk * (uint32_t)G * 4u;
 
   // LDS destinations are formed in the LDS address space from the array
   // itself (the load writes lane l's bytes at dst + l * size).
   lds_u8* const lds = (lds_u8*)smem;
-  const buf_rsrc rA = make_rsrc(Atile), rB = make_rsrc(Btile), rAs = make_rsrc(a_s), rBs = make_rsrc(b_s);
+  lds_u8* const cbuf = lds + RING_BYTES;
+  const buf_rsrc rA = make_rsrc(Atile), rB = make_rsrc(Btile), rBs = make_rsrc(b_s);
+  const buf_rsrc rAs = make_rsrc_n(a_s, (uint32_t)M * (uint32_t)G * 4u);
+  (void)ch_sub; (void)ch_i; (void)soff;
+  // Group g's tiles, b_s and (SCH = 0) a_s into ring slot st; with SCH = 1,
+  // part g mod CH of chunk g / CH + 1 (its images (g mod CH) * BM/64 ..)
+  // instead of a_s: by the time group CH * (g / CH + 1) is waited for, every
+  // part of its chunk has landed.
   auto issue = [&](int g, int st) {
     lds_u8* base = lds + st * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) lds_dma16(rA, aoff[i], g * kGroup, base + 1024 * (i * NW + wave));
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) lds_dma16(rB, boff[i], g * kGroup, base + A_BYTES + 1024 * (i * NW + wave));
-    lds_dma4(rAs, soff, 4 * g, base + A_BYTES + B_BYTES + 4 * ((wave * 64) % BM));
-    lds_dma4(rBs, bsoff, 4 * g, base + A_BYTES + B_BYTES + 4 * BM);
+    if constexpr (SCH) {
+      const int c = g / CH + 1, q = (g % CH) * (BM / 64) + wave % (BM / 64);
+      lds_dma4(rAs, as_off(q, c), 0, cbuf + (c % 3) * CB_BYTES + q * QSTRIDE);
+    } else {
+      lds_dma4(rAs, soff, 4 * g, base + A_BYTES + B_BYTES + 64 * 4 + 4 * ((wave * 64) % BM));
+    }
+    lds_dma4(rBs, bsoff, 4 * g, base + A_BYTES + B_BYTES);
   };
 
   v4f acc[IB][JB];
@@ -198,26 +250,36 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 #pragma unroll
     for (int r = 0; r < 4; ++r) a[r] = __builtin_fmaf(P[r], s, a[r]);
   };
-  // The partial of a group's last block is folded after the first MFMA of
-  // the next group (zero partial and zero scale before the first group).
-  v4f pp = v4f{0.f, 0.f, 0.f, 0.f};
-  float scp = 0.f;
+  // Each MFMA's partial is folded two MFMAs later (pp2: the partial of the
+  // MFMA before last, pp1: of the last one, with their scales), so a fold
+  // never waits for an MFMA still in the pipe.  The last two partials of a
+  // group are folded in the next group (zero partials and zero scales before
+  // the first group).
+  v4f pp1 = v4f{0.f, 0.f, 0.f, 0.f}, pp2 = pp1;
+  float sc1 = 0.f, sc2 = 0.f;
 
   // Head of a group: what its first MFMAs need, read from its LDS slot --
   // the lane's row scales, the b_s of the wave's columns, the first A
   // fragment (the B fragments are read one by one by the caller).
   float as[IB], bsv;
   v8i bf[JB], af;
-  auto read_head = [&](int st, float* as_o, float& bsv_o, v8i& af_o) {
+  auto read_head = [&](int st, int g, float* as_o, float& bsv_o, v8i& af_o) {
     const uint8_t* base = smem + st * STAGE_BYTES;
-    const float* sS = reinterpret_cast<const float*>(base + A_BYTES + B_BYTES);
-    bsv_o = sS[BM + (nb - (n0 >> 7))];
-    const v4f* ps = reinterpret_cast<const v4f*>(sS + (wm * 16 + (lane & 15)) * IB);
+    bsv_o = reinterpret_cast<const float*>(base + A_BYTES + B_BYTES)[nb - (n0 >> 7)];
+    if constexpr (SCH) {
+      const int b = wm * 16 + (lane & 15);
+      const float* cs = reinterpret_cast<const float*>(smem + RING_BYTES + ((g / CH) % 3) * CB_BYTES +
+                                                       (b / NBI) * QSTRIDE + (b % NBI) * CH * IB * 4) + g % CH;
 #pragma unroll
-    for (int q = 0; q < IB / 4; ++q) {
-      const v4f v = ps[q];
+      for (int i = 0; i < IB; ++i) as_o[i] = cs[CH * i];
+    } else {
+      const v4f* ps = reinterpret_cast<const v4f*>(base + A_BYTES + B_BYTES + 64 * 4) + (wm * 16 + (lane & 15)) * IB / 4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) as_o[4 * q + r] = v[r];
+      for (int q = 0; q < IB / 4; ++q) {
+        const v4f v = ps[q];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) as_o[4 * q + r] = v[r];
+      }
     }
     af_o = load_frag_lds_sw(base, wm * WM, lane);
   };
@@ -232,12 +294,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   // there lets the compiler sink every fold below it), and the number of
   // loads in flight is the same at every switch point.
   auto grp = [&](int g) { return g < G ? g : G - 1; };
+  // SCH = 1: chunk 0 up front, wave w loading images j*NW + w.
+  if constexpr (SCH) {
+#pragma unroll
+    for (int j = 0; j < CH / RF; ++j) lds_dma4(rAs, as_off(j * NW + wave, 0), 0, cbuf + (j * NW + wave) * QSTRIDE);
+  }
 #pragma unroll
   for (int p = 0; p < STAGES; ++p) issue(grp(p), p);
-  // Group 0 has landed once at most the later slots' loads are outstanding.
+  // Chunk 0 and group 0 have landed once at most the later slots' loads are
+  // outstanding.
   __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 1) * LPG));
   __builtin_amdgcn_s_barrier();
-  read_head(0, as, bsv, af);
+  read_head(0, 0, as, bsv, af);
 #pragma unroll
   for (int j = 0; j < JB; ++j) bf[j] = read_b(0, j);
 
@@ -263,24 +331,27 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
         __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 2) * LPG) & ~(15 << 8));
         __builtin_amdgcn_s_barrier();
         issue(grp(g + STAGES), st);
-        read_head(nst, as_n, bsv_n, af_n);
+        read_head(nst, g + 1, as_n, bsv_n, af_n);
       }
 #pragma unroll
       for (int j = 0; j < JB; ++j) {
-        // MFMA, then the previous partial's fold, in this order: left alone,
-        // the scheduler pulls each MFMA's own fold up next to it (to free
-        // registers early) and every fold stalls on its MFMA.
+        // MFMA, then the fold of the partial two MFMAs back (block k - 2 in
+        // the order k = i*JB + j, wrapping into the previous group), in this
+        // order: left alone, the scheduler pulls each MFMA's own fold up next
+        // to it (to free registers early) and every fold stalls on its MFMA.
         const v4f p = mfma_group(bf[j], af);
         __builtin_amdgcn_sched_barrier(0);
-        if (j == 0) fold(i == 0 ? acc[IB - 1][JB - 1] : acc[i - 1][JB - 1], pp, scp);
-        else fold(acc[i][j - 1], pp, sc);
+        const int k2 = (i * JB + j + IB * JB - 2) % (IB * JB);
+        fold(acc[k2 / JB][k2 % JB], pp2, sc2);
         // In the last block, B fragment j of the next group replaces this
         // one once its MFMA has been issued.
         if (i == IB - 1) bf[j] = read_b(nst, j);
         __builtin_amdgcn_sched_barrier(0);
-        pp = p;
+        pp2 = pp1;
+        sc2 = sc1;
+        pp1 = p;
+        sc1 = sc;
       }
-      scp = sc;
       if (i + 1 < IB) af = af_next;
     }
 #pragma unroll
@@ -288,7 +359,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
     bsv = bsv_n;
     af = af_n;
   }
-  fold(acc[IB - 1][JB - 1], pp, scp);
+  fold(acc[(IB * JB - 2) / JB][(IB * JB - 2) % JB], pp2, sc2);
+  fold(acc[IB - 1][JB - 1], pp1, sc1);
   // The refills issued past the last group must land before the workgroup
   // ends and its LDS is handed to another.
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
@@ -764,20 +836,20 @@ __global__ void k_fill_zero(void* __restrict__ C, int64_t count) {
 // ===========================================================================
 // Launchers
 // ===========================================================================
-template <int BM, int BN, int WM_, int WN_, int ST, int GRP>
+template <int BM, int BN, int WM_, int WN_, int ST, int SCH, int GRP>
 static hipError_t launch_generic_t(const GemmArgs& a, int64_t grid, int band, const int* offsets, int E) {
   const dim3 blk(64 * WM_ * WN_);
   switch (a.out) {
     case kOutBF16:
-      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutBF16, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, SCH, kOutBF16, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
                          a.B, a.b_s, a.C, a.M, a.N, a.K, band, a.vec, offsets, E);
       break;
     case kOutFP16:
-      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutFP16, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, SCH, kOutFP16, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
                          a.B, a.b_s, a.C, a.M, a.N, a.K, band, a.vec, offsets, E);
       break;
     default:
-      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, kOutFP32, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, SCH, kOutFP32, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
                          a.B, a.b_s, a.C, a.M, a.N, a.K, band, a.vec, offsets, E);
   }
   return hipGetLastError();
@@ -785,8 +857,8 @@ static hipError_t launch_generic_t(const GemmArgs& a, int64_t grid, int band, co
 
 hipError_t launch_generic(const GemmArgs& a, int cfg, int64_t grid, int band) {
   switch (cfg) {
-#define X(id, bm, bn, wm, wn, st) \
-  case id: return launch_generic_t<bm, bn, wm, wn, st, 0>(a, grid, band, nullptr, 0);
+#define X(id, bm, bn, wm, wn, st, sch) \
+  case id: return launch_generic_t<bm, bn, wm, wn, st, sch, 0>(a, grid, band, nullptr, 0);
     FBG_GENERIC_CFGS(X)
 #undef X
     default: return hipErrorInvalidValue;
@@ -795,8 +867,8 @@ hipError_t launch_generic(const GemmArgs& a, int cfg, int64_t grid, int band) {
 
 hipError_t launch_generic_grouped(const GemmArgs& a, int cfg, int64_t grid, const int* offsets, int E) {
   switch (cfg) {
-#define X(id, bm, bn, wm, wn, st) \
-  case id: return launch_generic_t<bm, bn, wm, wn, st, 1>(a, grid, 0, offsets, E);
+#define X(id, bm, bn, wm, wn, st, sch) \
+  case id: return launch_generic_t<bm, bn, wm, wn, st, sch, 1>(a, grid, 0, offsets, E);
     FBG_GENERIC_CFGS(X)
 #undef X
     default: return hipErrorInvalidValue;

@@ -37,8 +37,10 @@ int64_t skinny_tiles(const SkinnyCfg& c, int64_t M, int64_t N) {
 //
 // Swap-AB (small M): the smallest tile whose grid still fits the device in
 // one wave of workgroups -- 16 n x 16 m (config 2), else 32 n x 16 m
-// (config 7), else, for long K and M <= 64, 32 n x 64 m (config 19); none
-// fits -> the generic kernel.  Split over K only for K >= 2048, M > 1 and a
+// (config 7), else, for long K and M <= 64, 32 n x 64 m (config 19) where
+// its grid leaves room to split K in two; none fits -> the generic kernel,
+// whose 64 x 32 tiles beat an unsplit config 19 (N = 8192, K = 4096, M = 64:
+// 14.7 us against 18.0 us).  Split over K only for K >= 2048, M > 1 and a
 // grid of at most half the device.  (K = 1024, N = 512, M = 1: 2.85 us
 // unsplit 16x16 against 4.59 us for 32x16 split in two.)
 struct SwapPick {
@@ -58,7 +60,7 @@ bool swap_pick(int64_t M, int64_t N, int64_t G, int cu, SwapPick* out) {
   } else if (W7 <= cu) {
     out->cfg = 7;
     W = W7;
-  } else if (G >= 16 && M <= 64 && W19 <= cu) {
+  } else if (G >= 16 && M <= 64 && 2 * W19 <= cu) {
     out->cfg = 19;
     W = W19;
   } else {

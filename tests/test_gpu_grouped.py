@@ -66,6 +66,7 @@ GENERIC_GROUPED_CASES = [
     (13, [5] * 100, 200, 256),
     (14, [300, 1, 0, 257], 600, 640),
     (14, [256, 256], 257, 256),
+    (14, [130, 0, 3, 257], 300, 3200),
     (15, [65, 0, 64, 129, 3], 300, 2048),
     (15, [1] * 130, 140, 256),
     (16, [129, 0, 128, 1, 200], 260, 1024),

@@ -31,6 +31,10 @@ TOL_CASES = [
     ("generic", 2, 1, 130, 128, 0),
     ("generic", 3, 300, 520, 640, 0),
     ("generic", 3, 513, 257, 256, 0),
+    # 256x256 tile with row scales in 8-group chunks: several chunks, the
+    # three chunk buffers reused, a partial last chunk, ragged rows.
+    ("generic", 3, 300, 520, 3200, 0),
+    ("generic", 3, 257, 300, 2048, 0),
     ("generic", 4, 200, 300, 1024, 0),
     ("generic", 4, 64, 130, 512, 0),
     ("generic", 4, 1, 100, 256, 0),
@@ -110,6 +114,7 @@ EXACT_CASES = [
     ("generic", 0, 150, 300, 1024, 0),
     ("generic", 2, 40, 260, 512, 0),
     ("generic", 3, 260, 300, 768, 0),
+    ("generic", 3, 130, 260, 4224, 0),
     ("short_k256", 15, 100, 300, 256, 0),
     ("short_k256", 0, 100, 640, 256, 0),
     ("short_k256", 2, 5, 130, 256, 0),
