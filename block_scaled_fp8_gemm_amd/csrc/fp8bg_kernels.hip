@@ -320,6 +320,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
       v8i af_next;
       if (i + 1 < IB) af_next = load_frag_lds_sw(base, wm * WM + 16 * (i + 1), lane);
       sc = as[i] * bsv;
+      if (i == IB / 2) __builtin_amdgcn_s_setprio(0);
       if (i == IB - 1) {
         // Switch point: every LDS read of this group's slot has been issued.
         // Wait for them and for group g+1's loads (the later groups' loads
@@ -330,6 +331,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
         // values are never used.)
         __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 2) * LPG) & ~(15 << 8));
         __builtin_amdgcn_s_barrier();
+        // Wave priority 1 from here to the middle of the next group, 0 in its
+        // second half: of the two waves sharing a SIMD, one that has fallen
+        // behind gets the issue slots, so both reach the next barrier closer
+        // together (prefill 267 -> 260 us).
+        __builtin_amdgcn_s_setprio(1);
         issue(grp(g + STAGES), st);
         read_head(nst, g + 1, as_n, bsv_n, af_n);
       }
