@@ -455,10 +455,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 // skinny_reduce: sums the KW waves' partials through LDS in the fixed order
 // kw = 0..KW-1; wave w then owns blocks b with b % KW == w.
 // ===========================================================================
-template <int NB16, int MB16, int KW, int GPW, int KFIX>
+template <int NB16, int MB16, int KW, int GPW, int KFIX, int DMA = 0>
 __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint8_t* const* pa,
                                             const float* const* pas, const float* pbs, int g_lo, int g_hi, int kw,
-                                            int lane, v4f (&acc)[NB16][MB16]) {
+                                            int lane, v4f (&acc)[NB16][MB16],
+                                            const uint32_t (*pd)[2] = nullptr, const buf_rsrc* rsc = nullptr, uint8_t* stage = nullptr) {
   struct Chunk {
     v8i bf[GPW][NB16];
     v8i af[GPW][MB16];
@@ -470,16 +471,37 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
   // groups past the range are clamped (never computed).  Loads carry no
   // per-group condition, so the compiler counts outstanding loads exactly
   // and waits only for the chunk about to be used.
+  // DMA = 1: the fragments travel through this wave's LDS staging area
+  // instead (buffer c % 2; block b of group u -- weight blocks first, then
+  // activation blocks -- at ((c%2)*GPW + u)*NBK + b, 2 KB each, in the
+  // generic kernel's swizzled row layout).  Eight adjacent lanes then read
+  // one row's 128-byte group slice, so a load reaches the L1 as 64-byte
+  // accesses; a fragment load straight into registers reads 16 rows with
+  // 16 adjacent lanes and costs one access per lane.  pd[b][q] is this
+  // lane's offset, in resource rsc[b < NB16 ? 0 : 1], of rows 8q .. 8q+7 of
+  // block b (row 8q + lane/8 at its swizzled chunk).  The loads' completion
+  // is waited for by count: at most the next chunk's 2*NBK tile loads per
+  // group may stay in flight (the scale loads issued after them can only
+  // make this wait longer, never shorter).
+  constexpr int NBK = NB16 + MB16, LPC = GPW * 2 * NBK;
   auto load = [&](Chunk& ch, int c) {
     const int g0 = g_lo + (c * KW + kw) * GPW;
 #pragma unroll
     for (int u = 0; u < GPW; ++u) {
       const int g = (g0 + u) < g_hi ? (g0 + u) : (g_hi - 1);
       const int k0 = g * kGroup;
+      if constexpr (DMA) {
+        lds_u8* base = (lds_u8*)(stage + (((c & 1) * GPW + u) * NBK) * 2048);
 #pragma unroll
-      for (int i = 0; i < NB16; ++i) ch.bf[u][i] = load_frag_global(pb[i] + k0, lane);
+        for (int b = 0; b < NBK; ++b)
 #pragma unroll
-      for (int j = 0; j < MB16; ++j) ch.af[u][j] = load_frag_global(pa[j] + k0, lane);
+          for (int q = 0; q < 2; ++q) lds_dma16(rsc[b < NB16 ? 0 : 1], pd[b][q], k0, base + b * 2048 + q * 1024);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NB16; ++i) ch.bf[u][i] = load_frag_global(pb[i] + k0, lane);
+#pragma unroll
+        for (int j = 0; j < MB16; ++j) ch.af[u][j] = load_frag_global(pa[j] + k0, lane);
+      }
 #pragma unroll
       for (int j = 0; j < MB16; ++j) ch.as[u][j] = pas[j][g];
       ch.bs[u] = pbs[g];
@@ -491,8 +513,22 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
 #pragma unroll
     for (int j = 0; j < MB16; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Chunk& ch, int c) {
+  // pending: chunk c+1's loads were issued after chunk c's and may stay in
+  // flight (DMA form only; the register form is tracked by the compiler).
+  auto compute = [&](Chunk& ch, int c, bool pending) {
     const int g0 = g_lo + (c * KW + kw) * GPW;
+    if constexpr (DMA) {
+      if (pending) __builtin_amdgcn_s_waitcnt(vmcnt_only(LPC));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+#pragma unroll
+      for (int u = 0; u < GPW; ++u) {
+        const uint8_t* base = stage + (((c & 1) * GPW + u) * NBK) * 2048;
+#pragma unroll
+        for (int i = 0; i < NB16; ++i) ch.bf[u][i] = load_frag_lds_sw(base + i * 2048, 0, lane);
+#pragma unroll
+        for (int j = 0; j < MB16; ++j) ch.af[u][j] = load_frag_lds_sw(base + (NB16 + j) * 2048, 0, lane);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < GPW; ++u) {
       if (g0 + u < g_hi) {
@@ -517,7 +553,7 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
     if (my_chunks > 0) {
       Chunk ch;
       load(ch, 0);
-      compute(ch, 0);
+      compute(ch, 0, false);
     }
   } else if (my_chunks > 0) {
     // Two register buffers in ping-pong, no copies between them: chunk c+1
@@ -528,16 +564,16 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
     int c = 0;
     for (; c + 2 < my_chunks; c += 2) {
       load(b1, c + 1);
-      compute(b0, c);
+      compute(b0, c, true);
       load(b0, c + 2);
-      compute(b1, c + 1);
+      compute(b1, c + 1, true);
     }
     if (my_chunks - c == 2) {
       load(b1, c + 1);
-      compute(b0, c);
-      compute(b1, c + 1);
+      compute(b0, c, true);
+      compute(b1, c + 1, false);
     } else {
-      compute(b0, c);
+      compute(b0, c, false);
     }
   }
 
@@ -611,7 +647,13 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
   static_assert(128 % BN == 0, "a tile's n rows must share one b_s block");
   static_assert(KFIX == 0 || KW * GPW == KFIX, "the short-K form covers its groups in one chunk");
 
+  // Fragments through LDS (DMA) where the staging area (two chunks per
+  // wave) stays within 96 KB per workgroup; the short-K form loads straight
+  // into registers.
+  constexpr int STAGE_W = 2 * GPW * (NB16 + MB16) * 2048;
+  constexpr int DMA = KFIX == 0 && STAGE_W * KW <= 96 * 1024;
   __shared__ __attribute__((aligned(16))) float sRed[KW > 1 ? KW : 1][NBLK][4][64];
+  __shared__ __attribute__((aligned(16))) uint8_t sStage[DMA ? STAGE_W * KW : 16];
   __shared__ int sLast;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -651,9 +693,29 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
     pas[j] = a_s + (int64_t)r * G;
   }
   const float* pbs = b_s + (int64_t)nb * G;
+  // DMA sources: rows 8q + lane/8 of each 16-row block (clamped), at the
+  // row's swizzled 16-byte chunk, as 32-bit offsets from the tile's first
+  // weight row and first activation row.
+  const buf_rsrc rsc[2] = {make_rsrc(B + (int64_t)n0 * ldk), make_rsrc(A + (int64_t)m0 * ldk)};
+  uint32_t pd[NB16 + MB16][2];
+#pragma unroll
+  for (int b = 0; b < NB16 + MB16; ++b)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int rr = 8 * q + (lane >> 3);
+      const uint32_t chunk = 16u * (uint32_t)((lane & 7) ^ swz_row(rr));
+      if (b < NB16) {
+        const int r = 16 * b + rr;
+        pd[b][q] = (uint32_t)((n0 + r) < N ? r : (N - 1 - n0)) * (uint32_t)ldk + chunk;
+      } else {
+        const int r = 16 * (b - NB16) + rr;
+        pd[b][q] = (uint32_t)((m0 + r) < M ? r : (M - 1 - m0)) * (uint32_t)ldk + chunk;
+      }
+    }
 
   v4f acc[NB16][MB16];
-  skinny_tile<NB16, MB16, KW, GPW, KFIX>(pb, pa, pas, pbs, g_lo, g_hi, kw, lane, acc);
+  skinny_tile<NB16, MB16, KW, GPW, KFIX, DMA>(pb, pa, pas, pbs, g_lo, g_hi, kw, lane, acc, pd, rsc,
+                                              sStage + kw * (DMA ? STAGE_W : 0));
   // The KW waves' partials, summed in the fixed order kw = 0..KW-1; wave w
   // then owns blocks b with b % KW == w for the rest of the epilogue.
   skinny_reduce<NB16, MB16, KW>(sRed, kw, lane, acc);

@@ -35,14 +35,17 @@ int64_t skinny_tiles(const SkinnyCfg& c, int64_t M, int64_t N) {
 // costs ~1.5-2 us, more than splitting saves unless K is long and the
 // unsplit grid fills at most half the device.
 //
-// Swap-AB (small M): the smallest tile whose grid still fits the device in
-// one wave of workgroups -- 16 n x 16 m (config 2), else 32 n x 16 m
-// (config 7), else, for long K and M <= 64, 32 n x 64 m (config 19) where
-// its grid leaves room to split K in two; none fits -> the generic kernel,
-// whose 64 x 32 tiles beat an unsplit config 19 (N = 8192, K = 4096, M = 64:
-// 14.7 us against 18.0 us).  Split over K only for K >= 2048, M > 1 and a
-// grid of at most half the device.  (K = 1024, N = 512, M = 1: 2.85 us
-// unsplit 16x16 against 4.59 us for 32x16 split in two.)
+// Swap-AB (small M), its fragments staged through LDS: 16 n x 16 m tiles
+// (config 2) up to three workgroups per CU, else 32 n x 16 m (config 7) up to
+// two, else, for long K and M <= 64, 32 n x 64 m (config 19) where its grid
+// leaves room to split K in two; none fits -> the generic kernel.  Measured
+// (K = 4096): 16 x 16 beats 32 x 16 up to three workgroups per CU (N = 8192,
+// M = 16: 9.7 us against 10.2 us) and loses past it (N = 4096, M = 64: 13.3
+// us against 10.6 us); at two workgroups per CU the 32 x 16 tiles beat the
+// generic kernel (N = 512, M = 512: 9.7 us against 12.2 us), at three they
+// lose (N = 1536, M = 256: 15.8 us against 12.6 us).  Split over K only for
+// K >= 2048, M > 1 and a grid of at most half the device, into at most 4
+// (N = 512, M = 16: 5.8 us split in 8 against 5.4 us unsplit).
 struct SwapPick {
   int cfg;
   int64_t S;
@@ -51,13 +54,10 @@ struct SwapPick {
 bool swap_pick(int64_t M, int64_t N, int64_t G, int cu, SwapPick* out) {
   const int64_t W2 = cdiv(N, 16) * cdiv(M, 16), W7 = cdiv(N, 32) * cdiv(M, 16), W19 = cdiv(N, 32) * cdiv(M, 64);
   int64_t W;
-  // A single token (M = 1) keeps the 16x16 tiles at two workgroups per CU:
-  // its 16 clamped activation rows are one row, so a tile costs little more
-  // than its weight rows (N = 8192, K = 4096: 8.8 us against 9.3 us).
-  if (W2 <= cu || (M == 1 && W2 <= 2 * (int64_t)cu)) {
+  if (W2 <= 3 * (int64_t)cu) {
     out->cfg = 2;
     W = W2;
-  } else if (W7 <= cu) {
+  } else if (W7 <= 2 * (int64_t)cu) {
     out->cfg = 7;
     W = W7;
   } else if (G >= 16 && M <= 64 && 2 * W19 <= cu) {
@@ -75,7 +75,7 @@ bool swap_pick(int64_t M, int64_t N, int64_t G, int cu, SwapPick* out) {
     return true;
   }
   if (G >= 16 && M > 1 && 2 * W <= cu) {
-    const int64_t cap = G / kSwapCfgs[out->cfg].kw;
+    const int64_t cap = G / kSwapCfgs[out->cfg].kw < 4 ? G / kSwapCfgs[out->cfg].kw : 4;
     const int64_t want = cdiv(cu, W);
     out->S = want < cap ? want : cap;
     if (out->S < 1) out->S = 1;
@@ -189,7 +189,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
     // the generic kernel for the rest.
     if (K == 256 && M <= 1024)
       v = short_fits(M, N, cu) ? FBG_VARIANT_SHORT_K256 : FBG_VARIANT_GENERIC;
-    else if (M <= 16 || (M <= 256 && picked))
+    else if (M <= 16 || (M <= 512 && picked))
       v = FBG_VARIANT_SWAP_AB;
     else
       v = FBG_VARIANT_GENERIC;
