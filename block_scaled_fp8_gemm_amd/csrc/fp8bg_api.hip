@@ -41,6 +41,10 @@ bool env_flag(const char* name) {
 
 int elem_size(int out_dtype) { return out_dtype == FBG_OUT_FP32 ? 4 : 2; }
 
+// Largest K: the kernels address a tile's rows (up to 256 of K bytes each)
+// with 32-bit offsets from the tile's first row.
+constexpr int64_t kMaxK = (int64_t)1 << 24;
+
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -64,6 +68,8 @@ int validate(const void* A, const float* a_s, const void* B, const float* b_s, c
     return FBG_ERROR_INVALID_VALUE;
   if (K % 128 != 0) return FBG_ERROR_UNSUPPORTED;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return FBG_ERROR_UNSUPPORTED;
+  // The kernels address a tile's rows (up to 256 of them) with 32-bit offsets.
+  if (K > kMaxK) return FBG_ERROR_UNSUPPORTED;
   const int64_t G = K / 128, NB = (N + 127) / 128;
   const int64_t bytesA = M * K, bytesB = N * K, bytesAs = M * G * 4, bytesBs = NB * G * 4;
   const int64_t bytesC = M * N * elem_size(out_dtype);
@@ -242,6 +248,7 @@ extern "C" int fp8_block_gemm_grouped(const void* A, const float* a_s, const voi
     return FBG_ERROR_INVALID_VALUE;
   if (K % 128 != 0) return FBG_ERROR_UNSUPPORTED;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || E > INT32_MAX - 1) return FBG_ERROR_UNSUPPORTED;
+  if (K > kMaxK) return FBG_ERROR_UNSUPPORTED;  // 32-bit offsets inside a tile's rows
   const int64_t G = K / 128, NB = (N + 127) / 128;
   int64_t bytesB = 0, bytesBs = 0;
   if (__builtin_mul_overflow(E, N * K, &bytesB) || __builtin_mul_overflow(E, NB * G * 4, &bytesBs))

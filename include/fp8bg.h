@@ -90,8 +90,9 @@ typedef struct fbg_plan {
  * 16-byte aligned, a_s and b_s 4-byte aligned, C aligned to its element size.
  * A null pointer with a non-empty extent, a negative size, an unknown
  * out_dtype or a C range that overlaps an input range -> INVALID_VALUE;
- * K % 128 != 0, misalignment, M, N or K above INT32_MAX, or a scale array
- * of 4 GiB or more -> UNSUPPORTED.  When the chosen kernel splits
+ * K % 128 != 0, misalignment, M or N above INT32_MAX, K above 2^24 (the
+ * kernels' 32-bit offsets inside a tile's rows), or a scale array of 4 GiB
+ * or more -> UNSUPPORTED.  When the chosen kernel splits
  * K, its FP32 workspace is taken from a stream-ordered allocation on `stream`
  * (hipMallocAsync / hipFreeAsync), so concurrent calls on different streams
  * do not share it; failure -> OUT_OF_MEMORY before anything is launched.  Its
