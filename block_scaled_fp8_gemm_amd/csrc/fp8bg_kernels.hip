@@ -459,7 +459,8 @@ template <int NB16, int MB16, int KW, int GPW, int KFIX, int DMA = 0>
 __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint8_t* const* pa,
                                             const float* const* pas, const float* pbs, int g_lo, int g_hi, int kw,
                                             int lane, v4f (&acc)[NB16][MB16],
-                                            const uint32_t (*pd)[2] = nullptr, const buf_rsrc* rsc = nullptr, uint8_t* stage = nullptr) {
+                                            const uint32_t (*pd)[2] = nullptr, const buf_rsrc* rsc = nullptr, uint8_t* stage0 = nullptr,
+                                            uint8_t* stage1 = nullptr) {
   struct Chunk {
     v8i bf[GPW][NB16];
     v8i af[GPW][MB16];
@@ -471,10 +472,11 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
   // groups past the range are clamped (never computed).  Loads carry no
   // per-group condition, so the compiler counts outstanding loads exactly
   // and waits only for the chunk about to be used.
-  // DMA = 1: the fragments travel through this wave's LDS staging area
-  // instead (buffer c % 2; block b of group u -- weight blocks first, then
-  // activation blocks -- at ((c%2)*GPW + u)*NBK + b, 2 KB each, in the
-  // generic kernel's swizzled row layout).  Eight adjacent lanes then read
+  // DMA = 1: the fragments travel through this wave's LDS staging areas
+  // instead (stage0 with register buffer b0, stage1 with b1: two arrays, so
+  // the compiler sees that reading one does not wait for loads into the
+  // other; block b of group u -- weight blocks first, then activation blocks
+  // -- at u*NBK + b, 2 KB each, in the generic kernel's swizzled row layout).  Eight adjacent lanes then read
   // one row's 128-byte group slice, so a load reaches the L1 as 64-byte
   // accesses; a fragment load straight into registers reads 16 rows with
   // 16 adjacent lanes and costs one access per lane.  pd[b][q] is this
@@ -484,14 +486,14 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
   // group may stay in flight (the scale loads issued after them can only
   // make this wait longer, never shorter).
   constexpr int NBK = NB16 + MB16, LPC = GPW * 2 * NBK;
-  auto load = [&](Chunk& ch, int c) {
+  auto load = [&](Chunk& ch, int c, uint8_t* stage) {
     const int g0 = g_lo + (c * KW + kw) * GPW;
 #pragma unroll
     for (int u = 0; u < GPW; ++u) {
       const int g = (g0 + u) < g_hi ? (g0 + u) : (g_hi - 1);
       const int k0 = g * kGroup;
       if constexpr (DMA) {
-        lds_u8* base = (lds_u8*)(stage + (((c & 1) * GPW + u) * NBK) * 2048);
+        lds_u8* base = (lds_u8*)(stage + u * NBK * 2048);
 #pragma unroll
         for (int b = 0; b < NBK; ++b)
 #pragma unroll
@@ -515,14 +517,14 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
 
   // pending: chunk c+1's loads were issued after chunk c's and may stay in
   // flight (DMA form only; the register form is tracked by the compiler).
-  auto compute = [&](Chunk& ch, int c, bool pending) {
+  auto compute = [&](Chunk& ch, int c, bool pending, const uint8_t* stage) {
     const int g0 = g_lo + (c * KW + kw) * GPW;
     if constexpr (DMA) {
       if (pending) __builtin_amdgcn_s_waitcnt(vmcnt_only(LPC));
       else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
 #pragma unroll
       for (int u = 0; u < GPW; ++u) {
-        const uint8_t* base = stage + (((c & 1) * GPW + u) * NBK) * 2048;
+        const uint8_t* base = stage + u * NBK * 2048;
 #pragma unroll
         for (int i = 0; i < NB16; ++i) ch.bf[u][i] = load_frag_lds_sw(base + i * 2048, 0, lane);
 #pragma unroll
@@ -552,28 +554,28 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
   if constexpr (KFIX != 0) {
     if (my_chunks > 0) {
       Chunk ch;
-      load(ch, 0);
-      compute(ch, 0, false);
+      load(ch, 0, stage0);
+      compute(ch, 0, false, stage0);
     }
   } else if (my_chunks > 0) {
     // Two register buffers in ping-pong, no copies between them: chunk c+1
     // is in flight while chunk c is computed.  The steady-state loop runs
     // while two more chunks exist; the last one or two are peeled.
     Chunk b0, b1;
-    load(b0, 0);
+    load(b0, 0, stage0);
     int c = 0;
     for (; c + 2 < my_chunks; c += 2) {
-      load(b1, c + 1);
-      compute(b0, c, true);
-      load(b0, c + 2);
-      compute(b1, c + 1, true);
+      load(b1, c + 1, stage1);
+      compute(b0, c, true, stage0);
+      load(b0, c + 2, stage0);
+      compute(b1, c + 1, true, stage1);
     }
     if (my_chunks - c == 2) {
-      load(b1, c + 1);
-      compute(b0, c, true);
-      compute(b1, c + 1, false);
+      load(b1, c + 1, stage1);
+      compute(b0, c, true, stage0);
+      compute(b1, c + 1, false, stage1);
     } else {
-      compute(b0, c, false);
+      compute(b0, c, false, stage0);
     }
   }
 
@@ -650,10 +652,11 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
   // Fragments through LDS (DMA) where the staging area (two chunks per
   // wave) stays within 96 KB per workgroup; the short-K form loads straight
   // into registers.
-  constexpr int STAGE_W = 2 * GPW * (NB16 + MB16) * 2048;
-  constexpr int DMA = KFIX == 0 && STAGE_W * KW <= 96 * 1024;
+  constexpr int STAGE_H = GPW * (NB16 + MB16) * 2048;  // one chunk of one wave
+  constexpr int DMA = KFIX == 0 && 2 * STAGE_H * KW <= 96 * 1024;
   __shared__ __attribute__((aligned(16))) float sRed[KW > 1 ? KW : 1][NBLK][4][64];
-  __shared__ __attribute__((aligned(16))) uint8_t sStage[DMA ? STAGE_W * KW : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sStage0[DMA ? STAGE_H * KW : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sStage1[DMA ? STAGE_H * KW : 16];
   __shared__ int sLast;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -715,7 +718,7 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
 
   v4f acc[NB16][MB16];
   skinny_tile<NB16, MB16, KW, GPW, KFIX, DMA>(pb, pa, pas, pbs, g_lo, g_hi, kw, lane, acc, pd, rsc,
-                                              sStage + kw * (DMA ? STAGE_W : 0));
+                                              sStage0 + kw * (DMA ? STAGE_H : 0), sStage1 + kw * (DMA ? STAGE_H : 0));
   // The KW waves' partials, summed in the fixed order kw = 0..KW-1; wave w
   // then owns blocks b with b % KW == w for the rest of the epilogue.
   skinny_reduce<NB16, MB16, KW>(sRed, kw, lane, acc);

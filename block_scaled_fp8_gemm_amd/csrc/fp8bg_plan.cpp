@@ -44,8 +44,10 @@ int64_t skinny_tiles(const SkinnyCfg& c, int64_t M, int64_t N) {
 // us against 10.6 us); at two workgroups per CU the 32 x 16 tiles beat the
 // generic kernel (N = 512, M = 512: 9.7 us against 12.2 us), at three they
 // lose (N = 1536, M = 256: 15.8 us against 12.6 us).  Split over K only for
-// K >= 2048, M > 1 and a grid of at most half the device, into at most 4
-// (N = 512, M = 16: 5.8 us split in 8 against 5.4 us unsplit).
+// K >= 2048, M > 1 and a grid of at most three quarters of the device, into
+// enough splits for two workgroups per CU but at most 4 (decode N = 512,
+// M = 64: 6.17 us in 4 splits, 6.29 us in 2, 6.96 us unsplit; N = 512,
+// M = 128, one workgroup per CU unsplit: 6.35 us against 6.70 us in 2).
 struct SwapPick {
   int cfg;
   int64_t S;
@@ -74,9 +76,9 @@ bool swap_pick(int64_t M, int64_t N, int64_t G, int cu, SwapPick* out) {
     out->cfg = 11;
     return true;
   }
-  if (G >= 16 && M > 1 && 2 * W <= cu) {
+  if (G >= 16 && M > 1 && 4 * W <= 3 * (int64_t)cu) {
     const int64_t cap = G / kSwapCfgs[out->cfg].kw < 4 ? G / kSwapCfgs[out->cfg].kw : 4;
-    const int64_t want = cdiv(cu, W);
+    const int64_t want = cdiv(2 * (int64_t)cu, W);
     out->S = want < cap ? want : cap;
     if (out->S < 1) out->S = 1;
   }
