@@ -105,13 +105,14 @@ int swap_cfg_for(int64_t M, int64_t N, int64_t G, int cu) {
 }
 
 // Short-K (K == 256, two groups): 16 n x 16 m tiles with one group per wave
-// (config 12) while their grid fits two workgroups per CU; the automatic
+// (config 12) while their grid fits three workgroups per CU (N = 1536,
+// M = 128: 3.14 us against 3.34 us for the generic kernel); the automatic
 // dispatch sends larger shapes to the generic kernel (K = 256, N = 8192,
 // M = 512: 8.6 us against 13.0 us), and a forced short-K launch of such a
 // shape takes 32 n x 32 m (config 15) up to M = 200, 32 n x 64 m
 // (config 10) up to M = 256, else 32 n x 32 m with one wave taking both
 // groups (config 6).
-bool short_fits(int64_t M, int64_t N, int cu) { return cdiv(N, 16) * cdiv(M, 16) <= 2 * (int64_t)cu; }
+bool short_fits(int64_t M, int64_t N, int cu) { return cdiv(N, 16) * cdiv(M, 16) <= 3 * (int64_t)cu; }
 
 int short_cfg_for(int64_t M, int64_t N, int cu) {
   if (short_fits(M, N, cu) || M <= 48) return 12;
