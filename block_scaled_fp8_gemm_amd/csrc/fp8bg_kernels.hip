@@ -446,11 +446,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 // skinny_tile: this wave's FP32 partials of a workgroup tile of NB16 x MB16
 // 16x16 blocks (weight rows pb, activation rows pa with their a_s rows pas,
 // the tile's b_s block row pbs) over its chunks of the group range
-// [g_lo, g_hi).  Every wave loads its own B and A fragments straight from
-// global memory into registers, all loads of a chunk of GPW groups in flight
-// at once and the next chunk prefetched while the current one is computed.
-// The KW waves of a workgroup split the range: wave kw takes chunks kw,
-// kw+KW, ...
+// [g_lo, g_hi).  Every wave loads its own B and A fragments -- through its
+// own LDS staging area (DMA = 1) or straight into registers -- all loads of
+// a chunk of GPW groups in flight at once and the next chunk prefetched
+// while the current one is computed.  The KW waves of a workgroup split the
+// range: wave kw takes chunks kw, kw+KW, ...
 //
 // skinny_reduce: sums the KW waves' partials through LDS in the fixed order
 // kw = 0..KW-1; wave w then owns blocks b with b % KW == w.
@@ -616,10 +616,12 @@ __device__ __forceinline__ void skinny_reduce(Red& sRed, int kw, int lane, v4f (
 // operand, activation rows m (small M) on the second, so each lane ends with
 // 4 consecutive n of one output row m -- one vector store per block.
 //
-// Small-M shapes are latency- and bandwidth-bound, so operands are not staged
-// through LDS: every wave loads its own B and A fragments straight from
-// global memory into registers, all loads of a chunk of GPW groups in flight
-// at once and the next chunk prefetched while the current one is computed.
+// Small-M shapes are latency- and bandwidth-bound, so no workgroup-wide
+// operand tiles: every wave loads its own B and A fragments, through a
+// per-wave LDS staging area (coalesced 128-byte rows, no barriers) or, for
+// the largest tiles and the short-K form, straight into registers; all loads
+// of a chunk of GPW groups in flight at once and the next chunk prefetched
+// while the current one is computed.
 // The KW waves of a workgroup split the workgroup's K range (wave kw takes
 // chunks kw, kw+KW, ...); their FP32 partials are summed through LDS in the
 // fixed order kw = 0..KW-1.
