@@ -48,15 +48,28 @@ def test_plan_for_the_workloads():
     p = fbg.plan(64, 512, 4096)
     assert p["variant_name"] == "swap_ab_splitk" and p["split_k"] > 1 and p["workspace_bytes"] > 0
     assert p["grid"] >= 256
-    # K = 256: short-K while its 16x16 grid fits two workgroups per CU, the
+    # K = 256: short-K while its 16x16 grid fits three workgroups per CU, the
     # generic kernel beyond (measured faster there)
     assert fbg.plan(32, 4096, 256)["variant_name"] == "short_k256"
+    assert fbg.plan(128, 1536, 256)["variant_name"] == "short_k256"
     assert fbg.plan(184, 4096, 256)["variant_name"] == "generic"
     p = fbg.plan(128, 8192, 1024)
     assert p["variant_name"] in ("swap_ab", "swap_ab_splitk", "generic")
     # split-K only for long K with a grid of at most half the device
     assert fbg.plan(1, 512, 1024)["split_k"] == 1 and fbg.plan(64, 512, 1024)["split_k"] == 1
     assert fbg.plan(256, 512, 4096)["variant_name"] == "swap_ab"
+    # swap-AB tiles (their fragments staged through LDS) up to three 16x16 or
+    # two 32x16 workgroups per CU, the generic kernel past that (the measured
+    # dispatch sweep); decode splits K for two workgroups per CU, at most 4
+    p = fbg.plan(64, 512, 4096)
+    assert (p["config"], p["split_k"]) == (2, 4)
+    p = fbg.plan(128, 512, 4096)
+    assert p["variant_name"] == "swap_ab" and p["config"] == 2 and p["split_k"] == 1
+    p = fbg.plan(512, 512, 4096)
+    assert p["variant_name"] == "swap_ab" and p["config"] == 7
+    assert fbg.plan(128, 1536, 4096)["variant_name"] == "swap_ab"
+    assert fbg.plan(256, 1536, 4096)["variant_name"] == "generic"
+    assert fbg.plan(64, 8192, 4096)["variant_name"] == "generic"
     p = fbg.plan(16384, 4096, 4096)
     assert p["variant_name"] == "generic" and p["workspace_bytes"] == 0
 
