@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   constexpr int LPG = A_PER_T + B_PER_T + 2;         // vector-memory loads per group per thread
   // A ring slot holds a group's A and B tiles, its b_s (64 floats) and, with
   // SCH = 0, its row scales a_s (BM floats).
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, S_BYTES = 64 * 4 + (SCH ? 0 : BM * 4);
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, S_BYTES = 64 * 4 + (SCH ? 0 : BM * 4 + (NW > BM / 64 ? 64 * 4 : 0));
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES, RING_BYTES = STAGES * STAGE_BYTES;
   // With SCH = 1 the row scales travel in chunks of CH groups per row (CH * 4
   // contiguous bytes of a_s), three chunk buffers deep, outside the ring.  A
@@ -202,11 +202,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   // Row scales, SCH = 0: a_s of a group staged in its ring slot, transposed:
   // slot (w*16 + r)*IB + i holds row w*WM + 16*i + r, so the IB row scales a
   // lane needs (its row r = l & 15 in each of its wave's row blocks) are
-  // contiguous.  Wave w stages slots (64w mod BM) + lane: one load per row
-  // and group.
+  // contiguous.  Waves w < BM/64 stage slots 64w + lane: one load per row
+  // and group.  The other waves (their load keeps every wave's count per
+  // group equal) read one scale, the tile's first row's, into a spare 256
+  // bytes of the slot: one access instead of 64 more rows.
+  const bool s_spare = wave >= BM / 64;
   const int slot = (wave * 64) % BM + lane;
   const int srow = (slot / (16 * IB)) * WM + 16 * (slot % IB) + (slot / IB) % 16;
-  const int sr = (m0 + srow) < m_end ? (m0 + srow) : (m_end - 1);
+  const int sr = s_spare ? m0 : ((m0 + srow) < m_end ? (m0 + srow) : (m_end - 1));
   const uint32_t soff = (uint32_t)sr * (uint32_t)G * 4u;
   // b_s of the tile's column blocks (lane l holds block n0/128 + l, clamped to
   // the tile's last block), so the loop issues no scalar-memory loads.
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
       const int c = g / CH + 1, q = (g % CH) * (BM / 64) + wave % (BM / 64);
       lds_dma4(rAs, as_off(q, c), 0, cbuf + (c % 3) * CB_BYTES + q * QSTRIDE);
     } else {
-      lds_dma4(rAs, soff, 4 * g, base + A_BYTES + B_BYTES + 64 * 4 + 4 * ((wave * 64) % BM));
+      lds_dma4(rAs, soff, 4 * g, base + A_BYTES + B_BYTES + 64 * 4 + (s_spare ? 4 * BM : 4 * ((wave * 64) % BM)));
     }
     lds_dma4(rBs, bsoff, 4 * g, base + A_BYTES + B_BYTES);
   };
