@@ -46,8 +46,10 @@ int64_t skinny_tiles(const SkinnyCfg& c, int64_t M, int64_t N) {
 // lose (N = 1536, M = 256: 15.8 us against 12.6 us).  Split over K only for
 // K >= 2048, M > 1 and a grid of at most three quarters of the device, into
 // enough splits for two workgroups per CU but at most 4 (decode N = 512,
-// M = 64: 6.17 us in 4 splits, 6.29 us in 2, 6.96 us unsplit; N = 512,
-// M = 128, one workgroup per CU unsplit: 6.35 us against 6.70 us in 2).
+// M = 64: 6.13 us in 4 splits, 6.17 us in 2, 6.78 us unsplit; M = 32:
+// 5.74 us in 4 splits, 6.83 us unsplit; N = 512, M = 128, one workgroup per
+// CU unsplit: 6.79 us against 6.89 us in 2; the benchmark's back-to-back
+// replays over inputs rotated past the MALL).
 struct SwapPick {
   int cfg;
   int64_t S;
