@@ -625,6 +625,10 @@ def main():
                    "input_copies": r["copies"], "graphs": not args.no_graph},
         "roofline": roof,
     }
+    if args.cfg is not None:
+        # The plan call reports the automatic tile; a forced configuration's
+        # tile and grid are not known here.
+        line["config"].update(forced_cfg=args.cfg, tile=None, grid=None)
     fl = copy_floor_us(r["alg_bytes"], torch)
     line["copy_floor"] = {"us": round(fl, 3), "bytes": r["alg_bytes"],
                           "frac_of_floor": round(fl / (r["ms_per_step"] * 1e3), 4)}
