@@ -141,7 +141,9 @@ size_t fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int varian
  * shape by (M, N, K) to the best-fit kernel, with the generic kernel as the
  * fallback: section "Description").  Pure host code: makes no HIP call, so
  * it can run without a GPU.  variant / split_k force a choice as in
- * fp8_block_gemm_ex.  Returns SUCCESS and fills *out, or an error status.
+ * fp8_block_gemm_ex; FBG_FORCE_CONFIG is not read here (the plan shows the
+ * automatic tile configuration).  Returns SUCCESS and fills *out, or an
+ * error status.
  */
 int fp8_block_gemm_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count,
                         int variant, int split_k, fbg_plan *out);
