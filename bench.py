@@ -498,8 +498,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note "
-                                   "(N-, M- or K-sharding of the GEMM), not a measured path",
+        print(json.dumps({"error": "the library runs on one GPU; sharding the GEMM over several GPUs "
+                                   "(by N, M or K) is a design note, not a measured path",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
