@@ -9,7 +9,8 @@ namespace fbg {
 // Generic LDS-staged kernel: id, block tile BM x BN, waves WAVES_M x WAVES_N,
 // LDS ring depth in groups, row-scale staging (1: chunks of several groups
 // per row, loaded a few rows' runs per instruction; 0: one load per row and
-// group, staged in the ring slot).
+// group, staged in the ring slot).  Configuration 7 serves only the grouped
+// GEMM (experts of ~50-100 rows); the dense planner does not consider it.
 #define FBG_GENERIC_CFGS(X)  \
   X(0, 128, 128, 2, 2, 4, 0) \
   X(1, 256, 128, 2, 2, 3, 0) \
@@ -17,7 +18,8 @@ namespace fbg {
   X(3, 256, 256, 2, 4, 2, 1) \
   X(4, 64, 64, 1, 2, 4, 0)   \
   X(5, 128, 64, 2, 2, 3, 0)  \
-  X(6, 64, 32, 1, 2, 4, 0)
+  X(6, 64, 32, 1, 2, 4, 0)   \
+  X(7, 128, 256, 2, 4, 3, 0)
 
 // Skinny kernels (swap-AB and its split-K form): id, NB16 16-row blocks of
 // weight rows (output columns n), MB16 16-column blocks of activation rows
@@ -87,6 +89,7 @@ constexpr GenericCfg kGenericCfgs[] = {
 #undef X
 };
 constexpr int kNumGenericCfgs = sizeof(kGenericCfgs) / sizeof(kGenericCfgs[0]);
+constexpr int kNumDenseGenericCfgs = 7;  // configurations the dense planner chooses from
 
 struct SkinnyCfg { int nb16, mb16, kw, gpw; };
 constexpr SkinnyCfg kSwapCfgs[] = {

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   constexpr int RF = 64 * NW / BM;                   // loads of each image per chunk
   static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile images must split evenly over waves");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one b_s block");
-  static_assert(BM % 64 == 0 && (RF == 1 || RF == 2) && CH % RF == 0, "a chunk's images must split evenly over the waves");
+  static_assert(BM % 64 == 0 && (!SCH || RF == 1 || RF == 2) && CH % RF == 0, "a chunk's images must split evenly over the waves");
   static_assert(CH * IB <= 64 && 64 % (CH * IB) == 0, "a load image holds whole row classes");
   static_assert(SCH || IB == 4 || IB == 8, "a lane reads its row scales of a slot as one or two 16-byte words");
   static_assert(STAGES >= 2 && STAGES <= 4 && LDS_CU / (RING_BYTES + 3 * CB_BYTES) >= PER_CU, "LDS ring must fit in 160 KB");

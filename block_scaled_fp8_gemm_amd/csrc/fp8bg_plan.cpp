@@ -139,7 +139,7 @@ int64_t generic_cost(const GenericCfg& g, int64_t M, int64_t N, int cu) {
 
 int generic_cfg_for(int64_t M, int64_t N, int64_t G, int cu) {
   int best = 0;
-  for (int c = 1; c < kNumGenericCfgs; ++c) {
+  for (int c = 1; c < kNumDenseGenericCfgs; ++c) {
     const GenericCfg& g = kGenericCfgs[c];
     const GenericCfg& b = kGenericCfgs[best];
     const int64_t cg = generic_cost(g, M, N, cu), cb = generic_cost(b, M, N, cu);
@@ -266,12 +266,16 @@ int64_t workspace_bytes(const fbg_plan& p, int64_t M, int64_t N) {
 // of 512 x 4096, 16 .. 4096 tokens routed top-8).  Up to 12: 32-column tiles
 // of one 16-row block with the K range split over 8 waves (config 5: the
 // weight stream is the whole cost, and 8 waves keep the most loads in
-// flight); up to 20: 32 x 32 tiles (config 1); up to 96: 64-column tiles of
+// flight); up to 20: 32 x 32 tiles (config 1); up to 48: 64-column tiles of
 // up to 64 rows (config 6), which cut the activation re-reads (one per
 // column tile) 2x and stream each weight tile once for experts of up to 64
 // tokens.  Skinny tiles compute only their 16-row blocks that hold tokens.
-// Above 96 (prefill-sized experts), the generic kernel's 256 x 256 tiles in
-// grouped mode: 4096 tokens run in 289 us against 365 us.
+// Up to 96: the generic kernel's 128 x 256 tiles (8 waves, 3-slot ring) in
+// grouped mode, one row tile per expert (2048 tokens, 47-87 per expert:
+// 209.6 us against 222.7 us in config 6 and 231 us in 256 x 256); above
+// (prefill-sized experts), its 256 x 256 tiles: 4096 tokens run in 242 us
+// against 275 us in 128 x 256 (a second row tile re-reads the weight) and
+// 353-511 us in every other tile.
 int grouped_num_cfgs() { return kNumGroupedCfgs + kNumGenericCfgs; }
 int grouped_num_skinny_cfgs() { return kNumGroupedCfgs; }
 
@@ -282,8 +286,9 @@ int grouped_cfg_for(int64_t M, int64_t E, int64_t N, int64_t K, int force_cfg) {
   const int64_t per = E > 0 ? cdiv(M, E) : M;
   if (per <= 12) return 5;
   if (per <= 20) return 1;
-  if (per <= 96) return 6;
-  return kNumGroupedCfgs + 3;  // generic 256 x 256
+  if (per <= 48) return 6;
+  if (per <= 96) return kNumGroupedCfgs + 7;  // generic 128 x 256
+  return kNumGroupedCfgs + 3;                 // generic 256 x 256
 }
 
 int64_t grouped_grid(int cfg, int64_t E, int64_t M, int64_t N) {

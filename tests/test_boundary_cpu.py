@@ -294,6 +294,9 @@ def test_grouped_plan():
     # generic kernel, whose grid bounds the experts' row tiles by
     # ceil(M / BM) + E
     assert fbg.grouped_plan(256, 8192, 512, 4096)["tile_m"] > fbg.grouped_plan(256, 512, 512, 4096)["tile_m"]
+    p = fbg.grouped_plan(256, 16384, 512, 4096)   # ~64 rows per expert: 128 x 256 tiles
+    assert (p["tile_m"], p["tile_n"], p["waves"]) == (128, 256, 8)
+    assert p["grid"] == (-(-16384 // 128) + 256) * 2
     p = fbg.grouped_plan(256, 32768, 512, 4096)
     assert p["tile_m"] == 256 and p["waves"] == 8
     assert p["grid"] == (-(-32768 // 256) + 256) * -(-512 // p["tile_n"])

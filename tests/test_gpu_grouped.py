@@ -55,7 +55,7 @@ GROUPED_CASES = [
 
 # The generic kernel in grouped mode: configuration 11 + c runs generic tile
 # configuration c (BM x BN: 0 128x128, 1 256x128, 2 64x128, 3 256x256,
-# 4 64x64, 5 128x64, 6 64x32).  Experts spanning several row tiles, empty
+# 4 64x64, 5 128x64, 6 64x32, 7 128x256).  Experts spanning several row tiles, empty
 # experts, more than 64 experts (the tile scan's second chunk), ragged N.
 GENERIC_GROUPED_CASES = [
     (11, [130, 0, 1, 300, 7], 300, 1024),
@@ -73,6 +73,9 @@ GENERIC_GROUPED_CASES = [
     (16, [7, 0, 0, 300], 130, 384),
     (17, [65, 0, 64, 129, 3], 300, 1024),
     (17, [2] * 66, 130, 512),
+    (18, [65, 0, 64, 129, 3], 515, 1024),
+    (18, [130, 0, 3, 257], 300, 3200),
+    (18, [2] * 70, 260, 256),
 ]
 GROUPED_CASES = GROUPED_CASES + GENERIC_GROUPED_CASES
 

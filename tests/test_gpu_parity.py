@@ -43,6 +43,10 @@ TOL_CASES = [
     ("generic", 6, 130, 300, 1024, 0),
     ("generic", 6, 64, 33, 256, 0),
     ("generic", 6, 129, 260, 640, 0),
+    # 128x256 tile with 8 waves (grouped mid-size experts; forced here dense)
+    ("generic", 7, 300, 520, 1024, 0),
+    ("generic", 7, 129, 257, 384, 0),
+    ("generic", 7, 1, 600, 256, 0),
     ("short_k256", 0, 184, 700, 256, 0),
     ("short_k256", 0, 300, 515, 256, 0),
     ("short_k256", 1, 37, 130, 256, 0),
