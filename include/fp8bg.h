@@ -183,9 +183,12 @@ int fp8_block_gemm_grouped(const void *A, const float *a_s, const void *B, const
  * uses for E experts holding M token rows in total (chosen by the mean rows
  * per expert), as a plan: variant FBG_VARIANT_GROUPED, tile_m = the most
  * token rows a tile holds (a tile computes only its 16-row blocks that hold
- * tokens), tile_n, waves, config, grid = E * ceil(N / tile_n) workgroups
- * (those of empty experts exit at once), split_k 1, no workspace.  Pure host
- * code.  Negative sizes -> INVALID_VALUE; K % 128 != 0 -> UNSUPPORTED.
+ * tokens), tile_n, waves, config, split_k 1, no workspace; grid = E *
+ * ceil(N / tile_n) workgroups for the skinny tiles (those of empty experts
+ * exit at once), (ceil(M / tile_m) + E) * ceil(N / tile_n) for the generic
+ * kernel's tiles in grouped mode (the experts' row tiles fit in that bound;
+ * surplus workgroups exit at once).  Pure host code.  Negative sizes ->
+ * INVALID_VALUE; K % 128 != 0 -> UNSUPPORTED.
  */
 int fp8_block_gemm_grouped_plan(int64_t E, int64_t M, int64_t N, int64_t K, fbg_plan *out);
 
