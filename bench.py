@@ -4,23 +4,31 @@
 
 A step is one call of the whole hot path, fp8_block_gemm_ex (dispatcher +
 kernel, with split-K's fixed-order reduction inside the kernel), on one
-batch of synthetic input of the named workload (default: the decode shape
-M=64, N=512, K=4096, bf16 output).  Inputs sit in HBM before timing starts;
-consecutive steps rotate over enough input copies (> 2x the 256 MB MALL) that
-every step streams its operands from HBM, not from cache.  Steps are issued
-from HIP graphs (captured through torch) so that host launch cost does not
-hide the GPU time of a microsecond-scale kernel.  The timed region is
-bracketed by device synchronisation and by HIP events on the stream the
-kernels run on; ms_per_step and the roofline's per-launch duration come
-from those events.
+batch of synthetic input of the named workload (default: the prefill shape
+M=16384, N=4096, K=4096, bf16 output, the largest configuration of the
+metric; its N=1 line is the headline).  Inputs sit in HBM before timing
+starts.  Steps rotate over input copies such that between two uses of a copy
+the others move at least 2x the 256 MB MALL, and a scrub pass over 1 GiB of
+other memory separates the untimed steps from the timed ones, so every timed
+step reads its operands from HBM (step_schedule gives the exact order).
+Steps are issued from HIP graphs (captured through torch) so that host
+launch cost does not hide the GPU time of a microsecond-scale kernel.  The
+timed region is bracketed by device synchronisation and by HIP events on the
+stream the kernels run on; ms_per_step and the roofline's per-launch
+duration come from those events.
 
-Prints ONE JSON line (the benchmark contract), plus, on rank 0 at N=1, the
-CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line (the benchmark contract).  Its per_config key holds the
+metric's other configurations (the small, decode, short-K and mid-M shapes,
+the prefill shape with fp32 output, and the plain entry point fp8_block_gemm
+on the decode shape), each timed the same way; on rank 0 at N=1 it also
+carries the CPU oracle timed on a bounded sample of the same workload.
 
 Other modes (for profiles):
   --sweep FILE        every workload and sweep point, one JSON line each, to FILE
   --dispatch-sweep FILE   the dispatcher's choice against every forced alternative
                       on the pages' (M, N, K) shape sets, one JSON line per shape
+  --floors FILE       platform floors: a one-element kernel's launch-to-launch time
+                      in graph replays, and device copies of 0.25-256 MiB
   --copy-bytes B      only a plain device copy of B bytes (calibrates HBM counters)
   --op quantize       time the per-token 1x128 activation quantiser (bf16 -> E4M3
                       codes + fp32 scales) on the workload's A shape instead
@@ -28,6 +36,7 @@ Other modes (for profiles):
   --op grouped        the grouped (mixture-of-experts) GEMM on --moe NAME (default:
                       64 tokens routed top-8 over 256 experts of 512 x 4096)
   --no-graph          launch each step eagerly (for counter collection)
+  --no-per-config     only the named workload
 """
 import argparse
 import json
@@ -107,10 +116,64 @@ def make_device_copies(w, M, copies, torch, W):
     return d, sets
 
 
+def copies_for(per_copy, cap):
+    """Input copies to rotate over: enough that between two uses of one copy
+    the other copies move at least 2x the MALL (so every use reads HBM), at
+    most `cap`, at least 2."""
+    return max(2, min(cap, -(-2 * MALL_BYTES // per_copy) + 1))
+
+
+def chunk_sizes(steps, copies):
+    """The timed steps as graph replays: graphs of one pass over the copies
+    (or of all steps, if fewer), the last one shorter; they add up to `steps`."""
+    chunk = max(1, min(steps, copies))
+    return [chunk] * (steps // chunk) + ([steps % chunk] if steps % chunk else [])
+
+
+def step_schedule(copies, steps, warmup, use_graph):
+    """The order in which time_steps touches the input copies, as a list of
+    (phase, copy) pairs: phase "warm" (eager warm-up steps), "replay" (one
+    untimed replay of each captured graph), "scrub" (a pass over SCRUB_BYTES
+    of other memory, copy None) and "timed".  Pure; the CPU tests check on it
+    that every timed use of a copy comes at least 2x the MALL after its last
+    earlier use."""
+    ev = [("warm", i % copies) for i in range(warmup)]
+    if use_graph:
+        sizes = chunk_sizes(steps, copies)
+        for n in sorted(set(sizes)):
+            ev += [("replay", i) for i in range(n)]
+        ev.append(("scrub", None))
+        for n in sizes:
+            ev += [("timed", i) for i in range(n)]
+    else:
+        ev.append(("scrub", None))
+        ev += [("timed", i % copies) for i in range(steps)]
+    return ev
+
+
+SCRUB_BYTES = 4 * MALL_BYTES   # bytes a scrub pass moves (half read, half written)
+_scrub_bufs = []
+
+
+def scrub_mall(stream, torch):
+    """Evicts the MALL and the L2s: one device copy moving SCRUB_BYTES of
+    memory no step uses, on `stream`, then a device synchronisation."""
+    if not _scrub_bufs:
+        half = SCRUB_BYTES // 2
+        _scrub_bufs.extend([torch.ones(half, dtype=torch.uint8, device="cuda:0"),
+                            torch.empty(half, dtype=torch.uint8, device="cuda:0")])
+    with torch.cuda.stream(stream):
+        _scrub_bufs[1].copy_(_scrub_bufs[0], non_blocking=True)
+    torch.cuda.synchronize()
+
+
 def time_steps(step, copies, steps, warmup, use_graph, stream, torch):
     """Runs `warmup` untimed steps, then times exactly `steps` steps with HIP
-    events on `stream` (replayed from HIP graphs of one pass over the input
-    copies unless use_graph is false).  Returns (GPU ms, wall seconds)."""
+    events on `stream`, in the order step_schedule gives: replayed from HIP
+    graphs of one pass over the input copies (each graph replayed once,
+    untimed, first) unless use_graph is false, and preceded by a MALL scrub
+    so that no timed step finds its inputs in a cache.  Returns (GPU ms,
+    wall seconds)."""
     with torch.cuda.stream(stream):
         for i in range(warmup):
             step(i)
@@ -118,10 +181,7 @@ def time_steps(step, copies, steps, warmup, use_graph, stream, torch):
 
     plan_seq = []
     if use_graph:
-        # Each graph holds `chunk` consecutive steps (one pass over the input
-        # copies); the chunks executed add up to exactly `steps`.
-        chunk = min(steps, copies)
-        sizes = [chunk] * (steps // chunk) + ([steps % chunk] if steps % chunk else [])
+        sizes = chunk_sizes(steps, copies)
         graphs = {}
         for n in sorted(set(sizes)):
             g = torch.cuda.CUDAGraph()
@@ -131,12 +191,12 @@ def time_steps(step, copies, steps, warmup, use_graph, stream, torch):
             graphs[n] = g
         plan_seq = [graphs[n] for n in sizes]
         with torch.cuda.stream(stream):   # replay() launches on the current stream
-            for g in graphs.values():     # one untimed replay of each graph
-                g.replay()
+            for n in sorted(graphs):      # one untimed replay of each graph
+                graphs[n].replay()
         torch.cuda.synchronize()
+    scrub_mall(stream, torch)
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
         ev0.record(stream)
@@ -153,21 +213,31 @@ def time_steps(step, copies, steps, warmup, use_graph, stream, torch):
 
 
 def run_workload(args, w, M, out_name, torch, fbg, W, steps, warmup, use_graph=True,
-                 variant="auto", split_k=0, cfg=None):
+                 variant="auto", split_k=0, cfg=None, entry="ex", max_copies=None):
+    """Times `steps` GEMM calls on workload `w` at M rows.  entry "ex":
+    fp8_block_gemm_ex with a caller workspace (variant / split_k / cfg may
+    force a kernel); entry "fp8_block_gemm": the plain entry point with no
+    workspace, as a caller without one uses it."""
     out_dtype = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[out_name]
     out_bytes = 4 if out_name == "fp32" else 2
     N, K = w.N, w.K
     per_copy = M * K + N * K + 4 * M * (K // 128) + 4 * ((N + 127) // 128) * (K // 128) + M * N * out_bytes
-    copies = max(1, min(args.max_copies, -(-2 * MALL_BYTES // per_copy)))
+    copies = copies_for(per_copy, max_copies or args.max_copies)
     d, sets = make_device_copies(w, M, copies, torch, W)
     outs = [torch.empty((M, N), dtype=out_dtype, device="cuda:0") for _ in range(copies)]
     if cfg is not None:
         os.environ["FBG_FORCE_CONFIG"] = str(cfg)
-    plan = fbg.plan(M, N, K, out_dtype, torch.cuda.get_device_properties(0).multi_processor_count,
-                    variant, split_k)
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    if entry == "fp8_block_gemm":
+        assert variant == "auto" and split_k == 0 and cfg is None
+        plan = fbg.plan(M, N, K, out_dtype, cu, "auto", 1)   # no workspace: the unsplit plan
+        ws = "library"
+    else:
+        plan = fbg.plan(M, N, K, out_dtype, cu, variant, split_k)
+        ws = torch.zeros(max(fbg.workspace_size(M, N, K, variant, split_k), 16), dtype=torch.uint8,
+                         device="cuda:0")
     if cfg is not None:
         plan["config"] = cfg
-    ws = torch.zeros(max(fbg.workspace_size(M, N, K, variant, split_k), 16), dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.Stream()
 
     def step(i):
@@ -226,7 +296,7 @@ def run_quantize(args, w, M, torch, fbg, steps, warmup, use_graph=True, weights=
         bits = activation_bits(M, K, w.seed, w.outlier_frac, np)
         nbytes = quantize_bytes(M, K)
         srows = M
-    copies = max(1, min(args.max_copies, -(-2 * MALL_BYTES // nbytes)))
+    copies = copies_for(nbytes, args.max_copies)
     dev = torch.device("cuda:0")
     x0 = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
     xs = [x0] + [x0.clone() for _ in range(copies - 1)]
@@ -274,7 +344,7 @@ def run_grouped(args, mw, torch, fbg, W, steps, warmup, use_graph=True, out_name
         "offsets": torch.from_numpy(d["offsets"].astype(np.int32)).to(dev),
     }
     per_copy = sum(t.numel() * t.element_size() for t in base.values())
-    copies = max(2, min(args.max_copies, -(-2 * MALL_BYTES // per_copy)))
+    copies = copies_for(per_copy, args.max_copies)
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
     M, N = d["A"].shape[0], d["B"].shape[1]
     outs = [torch.empty((M, N), dtype=out_dtype, device=dev) for _ in range(copies)]
@@ -344,17 +414,29 @@ def host_cpu_model():
     return "unknown"
 
 
-def cpu_baseline(d, flops_per_call, budget_s=12.0, single_budget_s=4.0):
-    """The oracle as it stands, on the host's cores, repeated over the full
-    workload until about `budget_s` of CPU time has passed; then once more on
-    one thread for about `single_budget_s`."""
+def cpu_baseline(d, budget_s=12.0, single_budget_s=4.0, max_flops_per_call=20e9):
+    """The oracle as it stands, on the host's cores, repeated over the
+    workload until about `budget_s` has passed; then once more on one thread
+    for about `single_budget_s`.  A workload of more than `max_flops_per_call`
+    (the prefill shape: 550 GFLOP, over an hour for the fp64 oracle) is
+    sampled: the oracle computes its first rows only (every column, the whole
+    K), as many as fit in that bound; the rate is the same per row."""
     import oracle
-    oracle.block_gemm(d["A"][:1], d["a_s"][:1], d["B"], d["b_s"])  # load the library
+    A, a_s, B, b_s = d["A"], d["a_s"], d["B"], d["b_s"]
+    M, K = A.shape
+    N = B.shape[0]
+    rows = M
+    if 2 * M * N * K > max_flops_per_call:
+        rows = max(1, int(max_flops_per_call // (2 * N * K)))
+        rows = 1 << (rows.bit_length() - 1)      # a power of two
+        A, a_s = A[:rows], a_s[:rows]
+    flops_per_call = 2 * rows * N * K
+    oracle.block_gemm(A[:1], a_s[:1], B, b_s)  # load the library
 
     def timed(budget):
         reps, t0 = 0, time.perf_counter()
         while True:
-            oracle.block_gemm(d["A"], d["a_s"], d["B"], d["b_s"])
+            oracle.block_gemm(A, a_s, B, b_s)
             reps += 1
             el = time.perf_counter() - t0
             if el >= budget or reps >= 20000:
@@ -365,9 +447,10 @@ def cpu_baseline(d, flops_per_call, budget_s=12.0, single_budget_s=4.0):
     oracle.set_threads(1)
     reps1, el1 = timed(single_budget_s)
     oracle.set_threads(cores)
+    what = "full workload GEMM" if rows == M else f"rows 0..{rows - 1} of the workload (all {N} columns, K={K})"
     return {"value": round(reps * flops_per_call / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"full workload GEMM (fp64 oracle, E4M3 decode) repeated {reps}x in {el:.1f} s",
+            "sample": f"{what} (fp64 oracle, E4M3 decode) repeated {reps}x in {el:.1f} s",
             "value_1_thread": round(reps1 * flops_per_call / el1 / 1e12, 6), "cpu": host_cpu_model()}
 
 
@@ -396,7 +479,7 @@ def dispatch_sweep(path, torch, fbg, steps=100, warmup=10):
                 for M in (1, 16, 32, 64, 128, 256, 512, 1024, 4096):
                     G, NB = K // 128, (N + 127) // 128
                     per_copy = M * K + N * K + 4 * M * G + 4 * NB * G + 2 * M * N
-                    copies = max(1, min(256, -(-2 * MALL_BYTES // per_copy)))
+                    copies = copies_for(per_copy, 256)
                     base = {"A": codes(M, K), "B": codes(N, K),
                             "a_s": torch.rand((M, G), device=dev, generator=gen) * 0.01 + 1e-3,
                             "b_s": torch.rand((NB, G), device=dev, generator=gen) * 0.01 + 1e-3}
@@ -451,7 +534,7 @@ def copy_floor_us(nbytes, torch, steps=200, warmup=20):
     that reads nbytes/2 and writes nbytes/2, timed like the kernels (HIP-graph
     replays, buffers rotated past the MALL).  Returns microseconds per copy."""
     half = max(16, (nbytes // 2 + 15) // 16 * 16)
-    copies = max(2, min(256, -(-2 * MALL_BYTES // (2 * half))))
+    copies = copies_for(2 * half, 256)
     src = [torch.empty(half, dtype=torch.uint8, device="cuda:0").fill_(1) for _ in range(copies)]
     dst = [torch.empty(half, dtype=torch.uint8, device="cuda:0") for _ in range(copies)]
     stream = torch.cuda.Stream()
@@ -461,6 +544,28 @@ def copy_floor_us(nbytes, torch, steps=200, warmup=20):
 
     ms, _ = time_steps(step, copies, steps, warmup, True, stream, torch)
     return ms / steps * 1e3
+
+
+def platform_floors(path, torch):
+    """Launch and streaming floors of this GPU, timed like the kernels
+    (HIP-graph replays, buffers rotated past the MALL, scrubbed first): a
+    one-element fill (the launch-to-launch time of a kernel that does no
+    work) and device copies of 0.25 .. 256 MiB read + as many written."""
+    lines = []
+    one = [torch.empty(1, dtype=torch.float32, device="cuda:0") for _ in range(2)]
+    stream = torch.cuda.Stream()
+    ms, _ = time_steps(lambda i: one[i % 2].fill_(1.0), 2, 2000, 100, True, stream, torch)
+    lines.append({"floor": "launch", "what": "one-element fill kernel, back to back in a HIP graph",
+                  "us": round(ms / 2000 * 1e3, 3)})
+    for mib in (0.25, 1, 2, 8, 64, 256):
+        nbytes = int(2 * mib * (1 << 20))
+        us = copy_floor_us(nbytes, torch, steps=200 if mib < 64 else 20, warmup=10)
+        lines.append({"floor": "copy", "read_bytes": nbytes // 2, "written_bytes": nbytes // 2,
+                      "us": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    with open(path, "w") as f:
+        for line in lines:
+            f.write(json.dumps(line) + "\n")
+            print(json.dumps(line), flush=True)
 
 
 def copy_only(nbytes, torch, reps=5):
@@ -476,9 +581,12 @@ def copy_only(nbytes, torch, reps=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4096)
-    ap.add_argument("--warmup", type=int, default=256)
-    ap.add_argument("--workload", default="decode_64x512x4096")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 100 for the prefill shape, 4096 for the others)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default: 10 / 256)")
+    ap.add_argument("--workload", default="prefill_16384x4096x4096")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the named workload (the headline line without per_config)")
     ap.add_argument("--out", default=None, help="output dtype (default: the workload's first)")
     ap.add_argument("--M", type=int, default=None, help="a sweep point of the workload")
     ap.add_argument("--max-copies", type=int, default=1024)
@@ -487,6 +595,7 @@ def main():
     ap.add_argument("--sweep", default=None)
     ap.add_argument("--dispatch-sweep", default=None,
                     help="time the dispatcher's choice against every forced alternative on the pages' shape sets")
+    ap.add_argument("--floors", default=None, help="launch and streaming floors of the GPU, to FILE")
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--variant", default="auto", help="force a kernel variant (tuning)")
     ap.add_argument("--split", type=int, default=0, help="force a split-K count (tuning)")
@@ -515,6 +624,9 @@ def main():
 
     if args.dispatch_sweep:
         dispatch_sweep(args.dispatch_sweep, torch, fbg)
+        return
+    if args.floors:
+        platform_floors(args.floors, torch)
         return
     if args.sweep:
         with open(args.sweep, "w") as f:
@@ -552,6 +664,9 @@ def main():
                 print(json.dumps(line), flush=True)
         return
 
+    if args.op != "gemm":
+        args.steps = args.steps if args.steps is not None else 400
+        args.warmup = args.warmup if args.warmup is not None else 20
     if args.op == "grouped":
         mw = W.MOE_WORKLOADS[args.moe]
         out = args.out or "bf16"
@@ -602,7 +717,9 @@ def main():
         print(json.dumps(line), flush=True)
         return
     out = args.out or w.out_dtypes[0]
-    r = run_workload(args, w, M, out, torch, fbg, W, args.steps, args.warmup, not args.no_graph,
+    steps = args.steps if args.steps is not None else (100 if w.flops > 1e11 else 4096)
+    warmup = args.warmup if args.warmup is not None else (10 if w.flops > 1e11 else 256)
+    r = run_workload(args, w, M, out, torch, fbg, W, steps, warmup, not args.no_graph,
                      args.variant, args.split, args.cfg)
     roof = dict(r["roof"])
     roof["traffic"] = profiled_traffic(w.name, r["plan"], out) if args.cfg is None else None
@@ -611,8 +728,8 @@ def main():
         "value": round(r["tflops"], 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(r["ms_per_step"], 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -632,9 +749,51 @@ def main():
     fl = copy_floor_us(r["alg_bytes"], torch)
     line["copy_floor"] = {"us": round(fl, 3), "bytes": r["alg_bytes"],
                           "frac_of_floor": round(fl / (r["ms_per_step"] * 1e3), 4)}
+    d = r.pop("d")
+    del r
+    if not args.no_per_config and args.M is None and args.variant == "auto" and args.cfg is None:
+        line["per_config"] = per_config(args, w.name, out, torch, fbg, W)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(r["d"], 2 * M * w.N * w.K)
+        line["cpu_baseline"] = cpu_baseline(d)
     print(json.dumps(line), flush=True)
+
+
+# The other configurations of the metric (every (M,N,K) it is quoted on, and
+# the prefill shape's second output dtype), each timed like the headline, plus
+# the plain entry point fp8_block_gemm (no caller workspace) on the decode shape.
+PER_CONFIG = [("small_16x512x256", "bf16", "ex"), ("decode_64x512x4096", "bf16", "ex"),
+              ("decode_64x512x4096", "bf16", "fp8_block_gemm"), ("shortk_184x4096x256", "bf16", "ex"),
+              ("midm_128x8192x1024", "bf16", "ex"), ("prefill_16384x4096x4096", "bf16", "ex"),
+              ("prefill_16384x4096x4096", "fp32", "ex")]
+
+
+def per_config(args, head_name, head_out, torch, fbg, W):
+    """One entry per configuration of PER_CONFIG other than the headline's:
+    us per call, TFLOP/s, roofline fraction, and the fraction of a same-bytes
+    device copy.  Small shapes run 2000 steps over as many input copies (each
+    copy read once after the MALL scrub), the prefill shape 20."""
+    res = {}
+    for name, out, entry in PER_CONFIG:
+        if name == head_name and out == head_out and entry == "ex":
+            continue
+        w = W.WORKLOADS[name]
+        big = w.flops > 1e11
+        steps = 20 if big else 2000
+        r = run_workload(args, w, w.M, out, torch, fbg, W, steps, 5 if big else 50, not args.no_graph,
+                         entry=entry, max_copies=4 if big else 2048)
+        fl = copy_floor_us(r["alg_bytes"], torch)
+        key = f"{name}_{out}" + ("_fp8_block_gemm" if entry != "ex" else "")
+        res[key] = {"M": w.M, "N": w.N, "K": w.K, "out_dtype": out, "entry": entry,
+                    "variant": r["plan"]["variant_name"], "cfg": r["plan"]["config"],
+                    "split_k": r["plan"]["split_k"], "grid": r["plan"]["grid"], "steps": steps,
+                    "us": round(r["ms_per_step"] * 1e3, 3), "tflops": round(r["tflops"], 3),
+                    "roofline": dict(r["roof"], traffic=profiled_traffic(name, r["plan"], out)),
+                    "copy_floor_us": round(fl, 3),
+                    "frac_of_floor": round(fl / (r["ms_per_step"] * 1e3), 4)}
+        print(f"per_config {key}: {res[key]['us']} us", file=sys.stderr, flush=True)
+        del r
+        torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

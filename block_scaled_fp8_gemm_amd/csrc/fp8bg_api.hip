@@ -131,6 +131,11 @@ extern "C" int fp8_block_gemm_ex(const void* A, const float* a_s, const void* B,
   if (variant < FBG_VARIANT_AUTO || variant > FBG_VARIANT_SWAP_AB_SPLITK || split_k < 0)
     return FBG_ERROR_INVALID_VALUE;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
+  // No caller workspace and the dispatcher's choice: plan without a K split,
+  // so the call never allocates (a stream-ordered allocation and free cost
+  // more than splitting saves).  A split forced without a workspace still
+  // gets a stream-ordered one below.
+  if (!workspace && variant == FBG_VARIANT_AUTO && split_k == 0) split_k = 1;
   if (M == 0 || N == 0) return FBG_SUCCESS;
   if (K == 0) {
     // Still honour a forced variant's guard before filling.

@@ -118,6 +118,20 @@ def test_forced_variant_guards():
     assert fbg.plan(64, 512, 512, variant="generic")["variant_name"] == "generic"
 
 
+def test_automatic_plan_without_a_split():
+    # split_k = 1 under AUTO: the dispatcher's variant and tile with no K
+    # split -- the plan fp8_block_gemm (no caller workspace) runs, so that
+    # call never needs a workspace
+    for (M, N, K) in [(64, 512, 4096), (16, 1536, 4096), (32, 512, 4096), (1, 512, 256), (16384, 4096, 4096),
+                      (128, 8192, 1024), (300, 128, 2048)]:
+        p = fbg.plan(M, N, K, variant="auto", split_k=1)
+        assert p["split_k"] == 1 and p["workspace_bytes"] == 0, (M, N, K)
+        assert p["variant_name"] != "swap_ab_splitk"
+        q = fbg.plan(M, N, K)
+        if q["split_k"] == 1:
+            assert (p["variant_name"], p["config"]) == (q["variant_name"], q["config"]), (M, N, K)
+
+
 def test_workspace_size_for_forced_split():
     n = fbg.workspace_size(64, 512, 4096, "swap_ab_splitk", 8)
     p = fbg.plan(64, 512, 4096, variant="swap_ab_splitk", split_k=8)

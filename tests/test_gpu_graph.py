@@ -118,10 +118,35 @@ def test_quantizers_in_a_graph(gpu):
 
 
 def test_split_k_gemm_with_library_workspace_in_a_graph(gpu):
-    """fp8_block_gemm's own stream-ordered workspace (allocate, zero the
-    counters with a kernel, launch, free) captured as graph nodes."""
+    """A split forced without a caller workspace: the library's own
+    stream-ordered workspace (allocate, zero the counters with a kernel,
+    launch, free) captured as graph nodes."""
     M, N, K = 64, 512, 4096
     dd = to_dev(workloads.make_inputs(M, N, K, seed=32))
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+
+    def capture():
+        fbg.gemm(dd["A"], dd["a_s"], dd["B"], dd["b_s"], out=C, stream=torch.cuda.current_stream(),
+                 variant="swap_ab_splitk", split_k=4, workspace="library")
+        return [C]
+
+    def eager():
+        return [fbg.gemm(dd["A"], dd["a_s"], dd["B"], dd["b_s"], variant="swap_ab_splitk", split_k=4,
+                         workspace="library")]
+
+    def refill(i):
+        d = to_dev(workloads.make_inputs(M, N, K, seed=50 + i))
+        for k in dd:
+            dd[k].copy_(d[k])
+
+    replay_and_check(capture, eager, refill)
+
+
+def test_plain_entry_point_in_a_graph(gpu):
+    """fp8_block_gemm with no workspace (the unsplit plan: nothing to
+    allocate) captured and replayed."""
+    M, N, K = 64, 512, 4096
+    dd = to_dev(workloads.make_inputs(M, N, K, seed=34))
     C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
 
     def capture():
@@ -133,7 +158,7 @@ def test_split_k_gemm_with_library_workspace_in_a_graph(gpu):
         return [fbg.gemm(dd["A"], dd["a_s"], dd["B"], dd["b_s"], workspace="library")]
 
     def refill(i):
-        d = to_dev(workloads.make_inputs(M, N, K, seed=50 + i))
+        d = to_dev(workloads.make_inputs(M, N, K, seed=70 + i))
         for k in dd:
             dd[k].copy_(d[k])
 
