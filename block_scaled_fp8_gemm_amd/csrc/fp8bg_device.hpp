@@ -6,7 +6,7 @@
 // Operation (FlagGems-vllm PR #693, "feat: optimize w8a8 block fp8 matmul for
 // Hopper", section "Description"):
 //   C[m,n] = sum_g a_s[m,g] * b_s[n/128,g] * sum_{k in g} A[m,k] * B[n,k]
-// Every path accumulates in FP32 and casts to the output dtype (section
+// FP32 accumulation throughout, one rounding to the output type (section
 // "Numerical safety").
 #pragma once
 

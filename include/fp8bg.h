@@ -4,8 +4,8 @@
  * The operation (FlagGems-vllm PR #693, "feat: optimize w8a8 block fp8 matmul
  * for Hopper", section "Description": FP8 E4M3 activations with per-token
  * 1x128 scales, FP8 E4M3 weights with [block_n, block_k] = [128, 128] scales;
- * section "Numerical safety": every path accumulates in FP32 and casts to the
- * requested bf16 / fp16 / fp32 output):
+ * section "Numerical safety": FP32 accumulation on every kernel path, then one
+ * rounding to the bf16, fp16 or fp32 result):
  *
  *     C[m,n] = sum_g a_s[m,g] * b_s[n/128, g] * sum_{k = 128g}^{128g+127} A[m,k] * B[n,k]
  *
@@ -92,16 +92,11 @@ typedef struct fbg_plan {
  * out_dtype or a C range that overlaps an input range -> INVALID_VALUE;
  * K % 128 != 0, misalignment, M or N above INT32_MAX, K above 2^24 (the
  * kernels' 32-bit offsets inside a tile's rows), or a scale array of 4 GiB
- * or more -> UNSUPPORTED.  When the chosen kernel splits
- * K, its FP32 workspace is taken from a stream-ordered allocation on `stream`
- * (hipMallocAsync / hipFreeAsync), so concurrent calls on different streams
- * do not share it; failure -> OUT_OF_MEMORY before anything is launched.  Its
- * arrival counters are zeroed by a small kernel (no hipMemsetAsync), so the
- * call may be captured in a HIP graph as it is.  The stream-ordered
- * allocation and free cost ~15-20 us per split-K call on this GPU, eager or
- * captured (measured on 64x512x4096: 27 us eager, 22 us per graph replay,
- * against 7 us and 6 us with a caller workspace): latency-sensitive callers
- * pass their own workspace to fp8_block_gemm_ex.
+ * or more -> UNSUPPORTED.  The dispatcher's variant and tile are used
+ * without a K split (the plan of fp8_block_gemm_plan with split_k = 1), so
+ * the call needs no workspace and never allocates; it may be captured in a
+ * HIP graph as it is.  Callers that want the split-K plan where the
+ * dispatcher takes it pass a workspace to fp8_block_gemm_ex.
  */
 int fp8_block_gemm(const void *A, const float *a_s, const void *B, const float *b_s,
                    void *C, int64_t M, int64_t N, int64_t K, int out_dtype, void *stream);
@@ -115,8 +110,14 @@ int fp8_block_gemm(const void *A, const float *a_s, const void *B, const float *
  * split_k: 0 = the dispatcher's choice, else the number of K splits (only
  * SWAP_AB_SPLITK accepts > 1; it must not exceed K/128).
  * workspace / workspace_bytes: caller-owned device memory of at least
- * fp8_block_gemm_workspace_size(...) bytes, or NULL to let the library
- * allocate it stream-ordered.  The workspace holds FP32 partials and one
+ * fp8_block_gemm_workspace_size(...) bytes, or NULL.  With NULL, AUTO and
+ * split_k == 0 plan as fp8_block_gemm does (no K split, nothing allocated);
+ * a split forced without a workspace takes it from a stream-ordered
+ * allocation on `stream` (hipMallocAsync / hipFreeAsync, so concurrent calls
+ * on different streams never share one; its counters zeroed by a small
+ * kernel, no hipMemsetAsync; ~15-20 us per call, also as graph nodes under
+ * capture; failure -> OUT_OF_MEMORY before anything is launched).  The
+ * workspace holds FP32 partials and one
  * 32-bit arrival counter per output tile; the counters must be zero before
  * the first call that uses the buffer, and every completed call leaves them
  * zero again, so a buffer zeroed once can be reused by calls that are
