@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8bg.so")
 
-SUCCESS, INVALID_VALUE, UNSUPPORTED, OUT_OF_MEMORY, HIP_ERROR = 0, 1, 2, 3, 4
+SUCCESS, INVALID_VALUE, UNSUPPORTED, OUT_OF_MEMORY, HIP_ERROR, SCRATCH_LIMIT = 0, 1, 2, 3, 4, 5
 VARIANTS = {"auto": 0, "generic": 1, "short_k256": 2, "swap_ab": 3, "swap_ab_splitk": 4}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 VARIANT_NAMES[5] = "grouped"          # reported by grouped_plan only
@@ -56,6 +56,8 @@ def load():
     lib.fp8_block_gemm_ex.restype = _int
     lib.fp8_block_gemm_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp,
                                       _int, _int, _vp, _sz]
+    lib.fp8_block_gemm_noalloc.restype = _int
+    lib.fp8_block_gemm_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _int, _int]
     lib.fp8_block_gemm_workspace_size.restype = _sz
     lib.fp8_block_gemm_workspace_size.argtypes = [_i64, _i64, _i64, _int, _int]
     lib.fp8_block_gemm_plan.restype = _int
@@ -183,6 +185,36 @@ def gemm(A: torch.Tensor, a_s: torch.Tensor, B: torch.Tensor, b_s: torch.Tensor,
                                    M, N, K, code, s.cuda_stream, v, split_k, wp, wn)
     if st != SUCCESS:
         raise FP8BGError(st, "fp8_block_gemm")
+    return out
+
+
+def gemm_noalloc(A: torch.Tensor, a_s: torch.Tensor, B: torch.Tensor, b_s: torch.Tensor,
+                 out: torch.Tensor, variant="auto", split_k: int = 0,
+                 stream: torch.cuda.Stream = None) -> torch.Tensor:
+    """fp8_block_gemm_noalloc: the GEMM with any split-K partials in the
+    library's static per-GPU scratch, for callers that cannot allocate.  `out`
+    is required (this call allocates nothing, not even its output).  Calls
+    that overlap in time on one GPU share the scratch and must not be made;
+    see include/fp8bg.h."""
+    lib = load()
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape
+    N = B.shape[0]
+    G, NB = (K + 127) // 128, (N + 127) // 128
+    dev = A.device
+    _check(A, "A", FP8_DTYPES, (M, K), dev)
+    _check(B, "B", FP8_DTYPES, (N, K), dev)
+    _check(a_s, "a_s", (torch.float32,), (M, G), dev)
+    _check(b_s, "b_s", (torch.float32,), (NB, G), dev)
+    if out is None or out.dtype not in OUT_CODES:
+        raise ValueError("out must be a bf16 / fp16 / fp32 tensor")
+    _check(out, "out", (out.dtype,), (M, N), dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = lib.fp8_block_gemm_noalloc(A.data_ptr(), a_s.data_ptr(), B.data_ptr(), b_s.data_ptr(), out.data_ptr(),
+                                    M, N, K, OUT_CODES[out.dtype], s.cuda_stream, _variant_code(variant), split_k)
+    if st != SUCCESS:
+        raise FP8BGError(st, "fp8_block_gemm_noalloc")
     return out
 
 

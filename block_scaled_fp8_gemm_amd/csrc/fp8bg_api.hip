@@ -2,6 +2,7 @@
 // workspace handling and kernel launch.  See include/fp8bg.h for the
 // contract of each function.
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -95,7 +96,9 @@ int raster_band() {
   return b > 0 ? b : 8;
 }
 
-int launch_plan(const fbg_plan& p, const fbg::GemmArgs& args, void* ws, int64_t M, int64_t N) {
+// Launches the plan's kernel.  partial / counters: the split-K workspace's
+// FP32 partials and arrival counters (unused unless the plan splits K).
+int launch_plan(const fbg_plan& p, const fbg::GemmArgs& args, float* partial, unsigned* counters) {
   hipError_t e = hipSuccess;
   switch (p.variant) {
     case FBG_VARIANT_GENERIC:
@@ -105,27 +108,71 @@ int launch_plan(const fbg_plan& p, const fbg::GemmArgs& args, void* ws, int64_t 
       e = fbg::launch_short_k256(args, p.config, p.grid);
       break;
     case FBG_VARIANT_SWAP_AB:
-    case FBG_VARIANT_SWAP_AB_SPLITK: {
-      float* partial = nullptr;
-      unsigned* counters = nullptr;
-      if (p.split_k > 1) {
-        partial = static_cast<float*>(ws);
-        counters = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + fbg::workspace_counter_offset(p, M, N));
-      }
+    case FBG_VARIANT_SWAP_AB_SPLITK:
+      if (p.split_k <= 1) partial = nullptr, counters = nullptr;
       e = fbg::launch_swap(args, p.config, p.grid, p.split_k, partial, counters);
       break;
-    }
     default:
       return FBG_ERROR_INVALID_VALUE;
   }
   return e == hipSuccess ? FBG_SUCCESS : FBG_ERROR_HIP;
 }
 
-}  // namespace
+// A workspace laid out as fp8_block_gemm_workspace_size describes: the
+// partials first, the counters at workspace_counter_offset.
+int launch_with_workspace(const fbg_plan& p, const fbg::GemmArgs& args, void* ws, int64_t M, int64_t N) {
+  return launch_plan(p, args, static_cast<float*>(ws),
+                     reinterpret_cast<unsigned*>(static_cast<char*>(ws) + fbg::workspace_counter_offset(p, M, N)));
+}
 
-extern "C" int fp8_block_gemm_ex(const void* A, const float* a_s, const void* B, const float* b_s, void* C, int64_t M,
-                                 int64_t N, int64_t K, int out_dtype, void* stream_, int variant, int split_k,
-                                 void* workspace, size_t workspace_size) {
+// ---------------------------------------------------------------------------
+// The no-allocation entry point's scratch: split-K arrival counters in the
+// first kScratchCounterBytes, FP32 partials after them.  Every GPU the library
+// runs on holds its own copy for the life of the process.  In host code the
+// array's name is not a device address: the kernels get the per-device address
+// that hipGetSymbolAddress returns (scratch_address).  The counters are zero
+// when the code object is loaded, are cleared once more by the first call on
+// each device, and every completed call leaves them zero.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchBytes = (int64_t)4 << 20;
+constexpr int64_t kScratchCounterBytes = (int64_t)16 << 10;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// This device's scratch address (set up on the device's first call: the
+// symbol's address, then a kernel on `stream` clearing the counters), or
+// nullptr with *status set.
+void* scratch_address(hipStream_t stream, int* status) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = FBG_ERROR_HIP;
+    return nullptr;
+  }
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (ptr) return ptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+    (void)hipGetLastError();
+    *status = FBG_ERROR_HIP;
+    return nullptr;
+  }
+  if (fbg::launch_zero_words(ptr, kScratchCounterBytes / 4, stream) != hipSuccess) {
+    *status = FBG_ERROR_HIP;
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
+enum WorkspaceMode { kCallerOrLibrary, kStaticScratch };
+
+int gemm_call(const void* A, const float* a_s, const void* B, const float* b_s, void* C, int64_t M, int64_t N,
+              int64_t K, int out_dtype, void* stream_, int variant, int split_k, void* workspace,
+              size_t workspace_size, WorkspaceMode mode) {
   int st = validate(A, a_s, B, b_s, C, M, N, K, out_dtype);
   if (st != FBG_SUCCESS) return st;
   if (variant < FBG_VARIANT_AUTO || variant > FBG_VARIANT_SWAP_AB_SPLITK || split_k < 0)
@@ -134,8 +181,8 @@ extern "C" int fp8_block_gemm_ex(const void* A, const float* a_s, const void* B,
   // No caller workspace and the dispatcher's choice: plan without a K split,
   // so the call never allocates (a stream-ordered allocation and free cost
   // more than splitting saves).  A split forced without a workspace still
-  // gets a stream-ordered one below.
-  if (!workspace && variant == FBG_VARIANT_AUTO && split_k == 0) split_k = 1;
+  // gets a stream-ordered one below.  The static scratch keeps the split.
+  if (mode == kCallerOrLibrary && !workspace && variant == FBG_VARIANT_AUTO && split_k == 0) split_k = 1;
   if (M == 0 || N == 0) return FBG_SUCCESS;
   if (K == 0) {
     // Still honour a forced variant's guard before filling.
@@ -169,12 +216,22 @@ extern "C" int fp8_block_gemm_ex(const void* A, const float* a_s, const void* B,
             (long long)M, (long long)N, (long long)K, out_dtype, p.variant, p.config, p.tile_m, p.tile_n, p.split_k,
             (long long)p.grid, (long long)p.workspace_bytes);
 
-  if (p.workspace_bytes == 0) return launch_plan(p, args, nullptr, M, N);
+  if (p.workspace_bytes == 0) return launch_plan(p, args, nullptr, nullptr);
 
+  if (mode == kStaticScratch) {
+    const int64_t tiles = p.grid / p.split_k;
+    const int64_t partial = fbg::workspace_counter_offset(p, M, N);
+    if (tiles * 4 > kScratchCounterBytes || partial > kScratchBytes - kScratchCounterBytes)
+      return FBG_ERROR_SCRATCH_LIMIT;
+    char* base = static_cast<char*>(scratch_address(stream, &st));
+    if (!base) return st;
+    return launch_plan(p, args, reinterpret_cast<float*>(base + kScratchCounterBytes),
+                       reinterpret_cast<unsigned*>(base));
+  }
   if (workspace) {
     if (workspace_size < (size_t)p.workspace_bytes) return FBG_ERROR_OUT_OF_MEMORY;
     if (!aligned(workspace, 16)) return FBG_ERROR_UNSUPPORTED;
-    return launch_plan(p, args, workspace, M, N);
+    return launch_with_workspace(p, args, workspace, M, N);
   }
   // Library-owned workspace: stream-ordered, so concurrent streams never share one.
   if (env_flag("FBG_TEST_FAIL_ALLOC")) return FBG_ERROR_OUT_OF_MEMORY;
@@ -188,14 +245,29 @@ extern "C" int fp8_block_gemm_ex(const void* A, const float* a_s, const void* B,
     (void)hipFreeAsync(ws, stream);
     return FBG_ERROR_HIP;
   }
-  st = launch_plan(p, args, ws, M, N);
+  st = launch_with_workspace(p, args, ws, M, N);
   if (hipFreeAsync(ws, stream) != hipSuccess && st == FBG_SUCCESS) st = FBG_ERROR_HIP;
   return st;
+}
+
+}  // namespace
+
+extern "C" int fp8_block_gemm_ex(const void* A, const float* a_s, const void* B, const float* b_s, void* C, int64_t M,
+                                 int64_t N, int64_t K, int out_dtype, void* stream, int variant, int split_k,
+                                 void* workspace, size_t workspace_size) {
+  return gemm_call(A, a_s, B, b_s, C, M, N, K, out_dtype, stream, variant, split_k, workspace, workspace_size,
+                   kCallerOrLibrary);
 }
 
 extern "C" int fp8_block_gemm(const void* A, const float* a_s, const void* B, const float* b_s, void* C, int64_t M,
                               int64_t N, int64_t K, int out_dtype, void* stream) {
   return fp8_block_gemm_ex(A, a_s, B, b_s, C, M, N, K, out_dtype, stream, FBG_VARIANT_AUTO, 0, nullptr, 0);
+}
+
+extern "C" int fp8_block_gemm_noalloc(const void* A, const float* a_s, const void* B, const float* b_s, void* C,
+                                      int64_t M, int64_t N, int64_t K, int out_dtype, void* stream, int variant,
+                                      int split_k) {
+  return gemm_call(A, a_s, B, b_s, C, M, N, K, out_dtype, stream, variant, split_k, nullptr, 0, kStaticScratch);
 }
 
 extern "C" size_t fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int variant, int split_k) {

@@ -335,6 +335,8 @@ extern "C" const char* fp8_block_gemm_status_string(int status) {
     case FBG_ERROR_UNSUPPORTED: return "unsupported (K % 128 != 0, misaligned pointer, or a forced variant's guard failed)";
     case FBG_ERROR_OUT_OF_MEMORY: return "out of memory (split-K workspace unavailable or too small)";
     case FBG_ERROR_HIP: return "HIP runtime error";
+    case FBG_ERROR_SCRATCH_LIMIT:
+      return "scratch limit (the split-K partials or tile count exceed fp8_block_gemm_noalloc's 4 MiB static scratch)";
     default: return "unknown status";
   }
 }

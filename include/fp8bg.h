@@ -53,7 +53,8 @@ enum {
     FBG_ERROR_INVALID_VALUE = 1,  /* null pointer, negative size, bad dtype, C overlapping an input */
     FBG_ERROR_UNSUPPORTED = 2,    /* K % 128 != 0, misaligned pointer, a forced variant whose guard fails */
     FBG_ERROR_OUT_OF_MEMORY = 3,  /* split-K workspace could not be allocated / is too small */
-    FBG_ERROR_HIP = 4             /* a HIP runtime call or kernel launch failed */
+    FBG_ERROR_HIP = 4,            /* a HIP runtime call or kernel launch failed */
+    FBG_ERROR_SCRATCH_LIMIT = 5   /* fp8_block_gemm_noalloc: the split needs more than its static scratch */
 };
 
 /* Output dtypes. */
@@ -96,7 +97,8 @@ typedef struct fbg_plan {
  * without a K split (the plan of fp8_block_gemm_plan with split_k = 1), so
  * the call needs no workspace and never allocates; it may be captured in a
  * HIP graph as it is.  Callers that want the split-K plan where the
- * dispatcher takes it pass a workspace to fp8_block_gemm_ex.
+ * dispatcher takes it pass a workspace to fp8_block_gemm_ex, or use
+ * fp8_block_gemm_noalloc.
  */
 int fp8_block_gemm(const void *A, const float *a_s, const void *B, const float *b_s,
                    void *C, int64_t M, int64_t N, int64_t K, int out_dtype, void *stream);
@@ -126,6 +128,28 @@ int fp8_block_gemm(const void *A, const float *a_s, const void *B, const float *
 int fp8_block_gemm_ex(const void *A, const float *a_s, const void *B, const float *b_s,
                       void *C, int64_t M, int64_t N, int64_t K, int out_dtype, void *stream,
                       int variant, int split_k, void *workspace, size_t workspace_bytes);
+
+/*
+ * fp8_block_gemm_noalloc -- fp8_block_gemm_ex for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same operation, arguments, variant and
+ * split_k rules and statuses as fp8_block_gemm_ex, with the dispatcher's
+ * split-K plan kept (as with a caller workspace); the split's FP32 partials
+ * and arrival counters live in a static array of 4 MiB per GPU that the
+ * library holds until the process ends (16 KiB of counters -- at most 4096
+ * output tiles -- and the rest for partials; the automatic plans need at most
+ * ~0.7 MB).  The call never calls hipMalloc, hipFree or any allocating
+ * routine.  A split whose partials or tile count exceed the array ->
+ * FBG_ERROR_SCRATCH_LIMIT, nothing launched.  The first call on a device
+ * looks the array's address up and clears its counters with a kernel on
+ * `stream`; every completed call leaves them zero.  All calls on one GPU
+ * share its array: calls that overlap in time on one GPU (different streams,
+ * or a graph replayed concurrently with another call) race and must not be
+ * made; calls ordered on one stream are safe.
+ */
+int fp8_block_gemm_noalloc(const void *A, const float *a_s, const void *B, const float *b_s,
+                           void *C, int64_t M, int64_t N, int64_t K, int out_dtype, void *stream,
+                           int variant, int split_k);
 
 /*
  * fp8_block_gemm_workspace_size -- bytes of workspace fp8_block_gemm_ex needs

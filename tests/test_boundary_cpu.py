@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(5):
+    for st in range(6):
         assert len(fbg.status_string(st)) > 3
     assert fbg.status_string(99) == "unknown status"
 
