@@ -9,45 +9,55 @@ namespace fbg {
 // Generic LDS-staged kernel: id, block tile BM x BN, waves WAVES_M x WAVES_N,
 // LDS ring depth in groups, row-scale staging (1: chunks of several groups
 // per row, loaded a few rows' runs per instruction; 0: one load per row and
-// group, staged in the ring slot).  Configuration 7 serves only the grouped
-// GEMM (experts of ~50-100 rows); the dense planner does not consider it.
-#define FBG_GENERIC_CFGS(X)  \
-  X(0, 128, 128, 2, 2, 4, 0) \
-  X(1, 256, 128, 2, 2, 3, 0) \
-  X(2, 64, 128, 1, 2, 4, 0)  \
-  X(3, 256, 256, 2, 4, 2, 1) \
-  X(4, 64, 64, 1, 2, 4, 0)   \
-  X(5, 128, 64, 2, 2, 3, 0)  \
-  X(6, 64, 32, 1, 2, 4, 0)   \
-  X(7, 128, 256, 2, 4, 3, 0)
+// group, staged in the ring slot), mid-group refill (1: most of a group's
+// refill goes out after a second barrier in the middle of the group, spread
+// over several row blocks; the 256 x 256 tile).  Configuration 7 serves only
+// the grouped GEMM (experts of ~50-100 rows); the dense planner does not
+// consider it.  Configuration 8 (configuration 3 with the mid-group refill:
+// the dense planner takes it wherever it would take configuration 3) serves
+// only the dense planner; the grouped GEMM offers 0-7 (the mid-group refill
+// measured slower there: the 4096-token MoE workload 259 -> 305 us).
+#define FBG_GENERIC_CFGS(X)     \
+  X(0, 128, 128, 2, 2, 4, 0, 0) \
+  X(1, 256, 128, 2, 2, 3, 0, 0) \
+  X(2, 64, 128, 1, 2, 4, 0, 0)  \
+  X(3, 256, 256, 2, 4, 2, 1, 0) \
+  X(4, 64, 64, 1, 2, 4, 0, 0)   \
+  X(5, 128, 64, 2, 2, 3, 0, 0)  \
+  X(6, 64, 32, 1, 2, 4, 0, 0)   \
+  X(7, 128, 256, 2, 4, 3, 0, 0) \
+  X(8, 256, 256, 2, 4, 2, 1, 1)
 
 // Skinny kernels (swap-AB and its split-K form): id, NB16 16-row blocks of
 // weight rows (output columns n), MB16 16-column blocks of activation rows
 // (output rows m), KW waves splitting the workgroup's K range, GPW groups
-// per wave per chunk.
+// per wave per chunk, ONE: every wave stages its chunks through a single LDS
+// area, the whole chunk's loads in flight at once (configurations whose
+// KW * GPW groups cover a launch's K range, so a wave loads once, waits once).
 #define FBG_SWAP_CFGS(X) \
-  X(0, 1, 4, 4, 1)       \
-  X(1, 1, 4, 1, 2)       \
-  X(2, 1, 1, 4, 1)       \
-  X(3, 1, 2, 4, 1)       \
-  X(4, 2, 4, 2, 1)       \
-  X(5, 1, 8, 4, 1)       \
-  X(6, 4, 1, 4, 1)       \
-  X(7, 2, 1, 4, 1)       \
-  X(8, 1, 4, 2, 2)       \
-  X(9, 2, 2, 4, 1)       \
-  X(10, 1, 1, 16, 2)     \
-  X(11, 1, 1, 8, 2)      \
-  X(12, 2, 8, 4, 1)      \
-  X(13, 1, 8, 8, 1)      \
-  X(14, 1, 4, 8, 1)      \
-  X(15, 1, 2, 8, 2)      \
-  X(16, 2, 1, 8, 1)      \
-  X(17, 4, 1, 8, 1)      \
-  X(18, 1, 4, 4, 2)      \
-  X(19, 2, 4, 4, 1)      \
-  X(20, 1, 1, 4, 4)      \
-  X(21, 2, 1, 4, 2)
+  X(0, 1, 4, 4, 1, 0)    \
+  X(1, 1, 4, 1, 2, 0)    \
+  X(2, 1, 1, 4, 1, 0)    \
+  X(3, 1, 2, 4, 1, 0)    \
+  X(4, 2, 4, 2, 1, 0)    \
+  X(5, 1, 8, 4, 1, 0)    \
+  X(6, 4, 1, 4, 1, 0)    \
+  X(7, 2, 1, 4, 1, 0)    \
+  X(8, 1, 4, 2, 2, 0)    \
+  X(9, 2, 2, 4, 1, 0)    \
+  X(10, 1, 1, 16, 2, 0)  \
+  X(11, 1, 1, 8, 2, 0)   \
+  X(12, 2, 8, 4, 1, 0)   \
+  X(13, 1, 8, 8, 1, 0)   \
+  X(14, 1, 4, 8, 1, 0)   \
+  X(15, 1, 2, 8, 2, 0)   \
+  X(16, 2, 1, 8, 1, 0)   \
+  X(17, 4, 1, 8, 1, 0)   \
+  X(18, 1, 4, 4, 2, 0)   \
+  X(19, 2, 4, 4, 1, 0)   \
+  X(20, 1, 1, 4, 4, 0)   \
+  X(21, 2, 1, 4, 2, 0)   \
+  X(22, 1, 1, 8, 4, 1)
 
 // Short-K (K == 256, two groups, fully unrolled): same fields, KW * GPW == 2.
 #define FBG_SHORT_CFGS(X) \
@@ -82,18 +92,19 @@ namespace fbg {
   X(9, 4, 4, 4, 1)          \
   X(10, 8, 2, 2, 1)
 
-struct GenericCfg { int bm, bn, waves_m, waves_n, stages, scale_chunks; };
+struct GenericCfg { int bm, bn, waves_m, waves_n, stages, scale_chunks, mid_refill; };
 constexpr GenericCfg kGenericCfgs[] = {
-#define X(id, bm, bn, wm, wn, st, sch) {bm, bn, wm, wn, st, sch},
+#define X(id, bm, bn, wm, wn, st, sch, mid) {bm, bn, wm, wn, st, sch, mid},
     FBG_GENERIC_CFGS(X)
 #undef X
 };
 constexpr int kNumGenericCfgs = sizeof(kGenericCfgs) / sizeof(kGenericCfgs[0]);
-constexpr int kNumDenseGenericCfgs = 7;  // configurations the dense planner chooses from
+constexpr int kNumDenseGenericCfgs = 7;  // configurations the dense planner chooses from (0-6)
+constexpr int kNumGroupedGenericCfgs = 8;  // generic configurations the grouped GEMM may run (0-7)
 
-struct SkinnyCfg { int nb16, mb16, kw, gpw; };
+struct SkinnyCfg { int nb16, mb16, kw, gpw, one = 0; };
 constexpr SkinnyCfg kSwapCfgs[] = {
-#define X(id, nb, mb, kw, gpw) {nb, mb, kw, gpw},
+#define X(id, nb, mb, kw, gpw, one) {nb, mb, kw, gpw, one},
     FBG_SWAP_CFGS(X)
 #undef X
 };

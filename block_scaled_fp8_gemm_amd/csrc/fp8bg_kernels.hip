@@ -86,7 +86,7 @@ __device__ __forceinline__ void find_expert_tile(const int* offsets, int E, int 
 // that expert's weight, and clamps its rows to the expert's range instead of
 // to M.  Everything after the tile's placement is shared with the dense form.
 // ===========================================================================
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SCH, int OUT, int GRP>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SCH, int MID, int OUT, int GRP>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
     const uint8_t* __restrict__ A, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
     const float* __restrict__ b_s, void* __restrict__ C, int M, int N, int K, int band, int vec_ok,
@@ -117,8 +117,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   static_assert(BM % 64 == 0 && (!SCH || RF == 1 || RF == 2) && CH % RF == 0, "a chunk's images must split evenly over the waves");
   static_assert(CH * IB <= 64 && 64 % (CH * IB) == 0, "a load image holds whole row classes");
   static_assert(SCH || IB == 4 || IB == 8, "a lane reads its row scales of a slot as one or two 16-byte words");
-  static_assert(STAGES >= 2 && STAGES <= 4 && LDS_CU / (RING_BYTES + 3 * CB_BYTES) >= PER_CU, "LDS ring must fit in 160 KB");
+  static_assert(STAGES >= 2 && STAGES <= 8 && LDS_CU / (RING_BYTES + 3 * CB_BYTES) >= PER_CU, "LDS ring must fit in 160 KB");
   static_assert((STAGES - 1) * LPG + CH / RF < 64, "vmcnt counts at most 63 outstanding loads");
+  // MID = 1: a group's refill is split at a second barrier in the middle of
+  // the group.  By then every wave holds the group's B fragments (read at the
+  // previous switch point) and has read the A rows of its first IB/2 row
+  // blocks, so the B images, the b_s load and the A images covering those
+  // rows (A load i covers rows 64i .. 64i + 63, those of the first half of a
+  // wave row when i is even) refill the slot for group g + 2, spread over the
+  // next row blocks; only the other A images and the a_s load wait for the
+  // switch point.  Issuing all of a group's loads right after one barrier
+  // stalls the waves behind the address unit (prefill 288 -> 276 us bf16,
+  // 305 -> 294 us fp32, interleaved runs on one box).
+  constexpr int A_EARLY = MID ? A_PER_T / 2 : 0;
+  constexpr int N_MID = MID ? B_PER_T + 1 + A_EARLY : 0;  // loads per wave issued in the group's second half
+  static_assert(!MID || (SCH == 1 && STAGES == 2 && IB >= 6 && A_PER_T % 2 == 0 && WM == 64 * NW / 4 && NW == 8),
+                "the mid-group refill assumes the 256 x 256 tile's image-to-row-block mapping");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[RING_BYTES + 3 * CB_BYTES];
 
@@ -228,19 +242,40 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   // part g mod CH of chunk g / CH + 1 (its images (g mod CH) * BM/64 ..)
   // instead of a_s: by the time group CH * (g / CH + 1) is waited for, every
   // part of its chunk has landed.
+  // MID: load j of the mid-group part (B images, b_s, even A images).
+  auto issue_mid = [&](int g, int st, int j) {
+    lds_u8* base = lds + st * STAGE_BYTES;
+    if (j < B_PER_T) lds_dma16(rB, boff[j], g * kGroup, base + A_BYTES + 1024 * (j * NW + wave));
+    else if (j == B_PER_T) lds_dma4(rBs, bsoff, 4 * g, base + A_BYTES + B_BYTES);
+    else {
+      const int i = 2 * (j - B_PER_T - 1);
+      lds_dma16(rA, aoff[i], g * kGroup, base + 1024 * (i * NW + wave));
+    }
+  };
   auto issue = [&](int g, int st) {
     lds_u8* base = lds + st * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) lds_dma16(rA, aoff[i], g * kGroup, base + 1024 * (i * NW + wave));
+    for (int i = 0; i < A_PER_T; ++i)
+      if (!MID || (i & 1)) lds_dma16(rA, aoff[i], g * kGroup, base + 1024 * (i * NW + wave));
+    if constexpr (!MID) {
 #pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) lds_dma16(rB, boff[i], g * kGroup, base + A_BYTES + 1024 * (i * NW + wave));
+      for (int i = 0; i < B_PER_T; ++i) lds_dma16(rB, boff[i], g * kGroup, base + A_BYTES + 1024 * (i * NW + wave));
+    }
     if constexpr (SCH) {
       const int c = g / CH + 1, q = (g % CH) * (BM / 64) + wave % (BM / 64);
       lds_dma4(rAs, as_off(q, c), 0, cbuf + (c % 3) * CB_BYTES + q * QSTRIDE);
     } else {
       lds_dma4(rAs, soff, 4 * g, base + A_BYTES + B_BYTES + 64 * 4 + (s_spare ? 4 * BM : 4 * ((wave * 64) % BM)));
     }
-    lds_dma4(rBs, bsoff, 4 * g, base + A_BYTES + B_BYTES);
+    if constexpr (!MID) lds_dma4(rBs, bsoff, 4 * g, base + A_BYTES + B_BYTES);
+  };
+  // Both parts (the prologue's full groups).
+  auto issue_all = [&](int g, int st) {
+    if constexpr (MID) {
+#pragma unroll
+      for (int j = 0; j < N_MID; ++j) issue_mid(g, st, j);
+    }
+    issue(g, st);
   };
 
   v4f acc[IB][JB];
@@ -303,7 +338,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
     for (int j = 0; j < CH / RF; ++j) lds_dma4(rAs, as_off(j * NW + wave, 0), 0, cbuf + (j * NW + wave) * QSTRIDE);
   }
 #pragma unroll
-  for (int p = 0; p < STAGES; ++p) issue(grp(p), p);
+  for (int p = 0; p < STAGES; ++p) issue_all(grp(p), p);
   // Chunk 0 and group 0 have landed once at most the later slots' loads are
   // outstanding.
   __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 1) * LPG));
@@ -324,6 +359,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
       if (i + 1 < IB) af_next = load_frag_lds_sw(base, wm * WM + 16 * (i + 1), lane);
       sc = as[i] * bsv;
       if (i == IB / 2) __builtin_amdgcn_s_setprio(0);
+      if constexpr (MID) {
+        // Mid-group barrier: the slot's B region and the A rows of the first
+        // IB/2 row blocks are no longer read by any wave; their refill for
+        // group g + 2 goes out over row blocks IB/2 .. IB-2.
+        if (i == IB / 2) __builtin_amdgcn_s_barrier();
+        if (i >= IB / 2 && i <= IB - 2) {
+          constexpr int NB = IB / 2 - 1;
+#pragma unroll
+          for (int j = 0; j < N_MID; ++j)
+            if (j * NB / N_MID == i - IB / 2) issue_mid(grp(g + STAGES), st, j);
+        }
+      }
       if (i == IB - 1) {
         // Switch point: every LDS read of this group's slot has been issued.
         // Wait for them and for group g+1's loads (the later groups' loads
@@ -332,7 +379,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
         // g + STAGES, and read g+1's head while this block's MFMAs run.
         // (After the last group the head reads fetch a stale slot; the
         // values are never used.)
-        __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 2) * LPG) & ~(15 << 8));
+        __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 2) * LPG + N_MID) & ~(15 << 8));
         __builtin_amdgcn_s_barrier();
         // Wave priority 1 from here to the middle of the next group, 0 in its
         // second half: of the two waves sharing a SIMD, one that has fallen
@@ -458,7 +505,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 // skinny_reduce: sums the KW waves' partials through LDS in the fixed order
 // kw = 0..KW-1; wave w then owns blocks b with b % KW == w.
 // ===========================================================================
-template <int NB16, int MB16, int KW, int GPW, int KFIX, int DMA = 0>
+template <int NB16, int MB16, int KW, int GPW, int KFIX, int DMA = 0, int ONE = 0>
 __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint8_t* const* pa,
                                             const float* const* pas, const float* pbs, int g_lo, int g_hi, int kw,
                                             int lane, v4f (&acc)[NB16][MB16],
@@ -560,6 +607,16 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
       load(ch, 0, stage0);
       compute(ch, 0, false, stage0);
     }
+  } else if constexpr (ONE) {
+    // One staging area: each chunk's loads all in flight, one wait, then its
+    // MFMAs (the configurations are chosen so one chunk covers the range).
+    // The area is refilled only after the previous chunk's fragments are in
+    // registers (its MFMAs consumed them).
+    for (int c = 0; c < my_chunks; ++c) {
+      Chunk ch;
+      load(ch, c, stage0);
+      compute(ch, c, false, stage0);
+    }
   } else if (my_chunks > 0) {
     // Two register buffers in ping-pong, no copies between them: chunk c+1
     // is in flight while chunk c is computed.  The steady-state loop runs
@@ -643,7 +700,7 @@ __device__ __forceinline__ void skinny_reduce(Red& sRed, int kw, int lane, v4f (
 // groups once per tile (b_s folded into a_s) and the two partials combine as
 // fma(P1, s1, fma(P0, s0, 0)).
 // ===========================================================================
-template <int NB16, int MB16, int KW, int GPW, int KFIX, int OUT>
+template <int NB16, int MB16, int KW, int GPW, int KFIX, int ONE, int OUT>
 __global__ __launch_bounds__(64 * KW) void k_skinny(
     const uint8_t* __restrict__ A, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
     const float* __restrict__ b_s, void* __restrict__ C, int M, int N, int K, int S,
@@ -654,14 +711,16 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
   static_assert(128 % BN == 0, "a tile's n rows must share one b_s block");
   static_assert(KFIX == 0 || KW * GPW == KFIX, "the short-K form covers its groups in one chunk");
 
-  // Fragments through LDS (DMA) where the staging area (two chunks per
-  // wave) stays within 96 KB per workgroup; the short-K form loads straight
-  // into registers.
+  // Fragments through LDS (DMA) where the staging area stays within 96 KB
+  // per workgroup for two chunks per wave, or 128 KB for one (ONE, and the
+  // short-K form, whose one chunk holds both groups); the other
+  // configurations load straight into registers.
   constexpr int STAGE_H = GPW * (NB16 + MB16) * 2048;  // one chunk of one wave
-  constexpr int DMA = KFIX == 0 && 2 * STAGE_H * KW <= 96 * 1024;
+  constexpr int SINGLE = ONE || KFIX != 0;
+  constexpr int DMA = SINGLE ? STAGE_H * KW <= 128 * 1024 : 2 * STAGE_H * KW <= 96 * 1024;
   __shared__ __attribute__((aligned(16))) float sRed[KW > 1 ? KW : 1][NBLK][4][64];
   __shared__ __attribute__((aligned(16))) uint8_t sStage0[DMA ? STAGE_H * KW : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t sStage1[DMA ? STAGE_H * KW : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sStage1[DMA && !SINGLE ? STAGE_H * KW : 16];
   __shared__ int sLast;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -722,8 +781,9 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
     }
 
   v4f acc[NB16][MB16];
-  skinny_tile<NB16, MB16, KW, GPW, KFIX, DMA>(pb, pa, pas, pbs, g_lo, g_hi, kw, lane, acc, pd, rsc,
-                                              sStage0 + kw * (DMA ? STAGE_H : 0), sStage1 + kw * (DMA ? STAGE_H : 0));
+  skinny_tile<NB16, MB16, KW, GPW, KFIX, DMA, ONE>(pb, pa, pas, pbs, g_lo, g_hi, kw, lane, acc, pd, rsc,
+                                                   sStage0 + kw * (DMA ? STAGE_H : 0),
+                                                   sStage1 + kw * (DMA && !SINGLE ? STAGE_H : 0));
   // The KW waves' partials, summed in the fixed order kw = 0..KW-1; wave w
   // then owns blocks b with b % KW == w for the rest of the epilogue.
   skinny_reduce<NB16, MB16, KW>(sRed, kw, lane, acc);
@@ -912,20 +972,20 @@ __global__ void k_fill_zero(void* __restrict__ C, int64_t count) {
 // ===========================================================================
 // Launchers
 // ===========================================================================
-template <int BM, int BN, int WM_, int WN_, int ST, int SCH, int GRP>
+template <int BM, int BN, int WM_, int WN_, int ST, int SCH, int MID, int GRP>
 static hipError_t launch_generic_t(const GemmArgs& a, int64_t grid, int band, const int* offsets, int E) {
   const dim3 blk(64 * WM_ * WN_);
   switch (a.out) {
     case kOutBF16:
-      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, SCH, kOutBF16, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, SCH, MID, kOutBF16, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
                          a.B, a.b_s, a.C, a.M, a.N, a.K, band, a.vec, offsets, E);
       break;
     case kOutFP16:
-      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, SCH, kOutFP16, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, SCH, MID, kOutFP16, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
                          a.B, a.b_s, a.C, a.M, a.N, a.K, band, a.vec, offsets, E);
       break;
     default:
-      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, SCH, kOutFP32, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+      hipLaunchKernelGGL((k_generic<BM, BN, WM_, WN_, ST, SCH, MID, kOutFP32, GRP>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
                          a.B, a.b_s, a.C, a.M, a.N, a.K, band, a.vec, offsets, E);
   }
   return hipGetLastError();
@@ -933,8 +993,8 @@ static hipError_t launch_generic_t(const GemmArgs& a, int64_t grid, int band, co
 
 hipError_t launch_generic(const GemmArgs& a, int cfg, int64_t grid, int band) {
   switch (cfg) {
-#define X(id, bm, bn, wm, wn, st, sch) \
-  case id: return launch_generic_t<bm, bn, wm, wn, st, sch, 0>(a, grid, band, nullptr, 0);
+#define X(id, bm, bn, wm, wn, st, sch, mid) \
+  case id: return launch_generic_t<bm, bn, wm, wn, st, sch, mid, 0>(a, grid, band, nullptr, 0);
     FBG_GENERIC_CFGS(X)
 #undef X
     default: return hipErrorInvalidValue;
@@ -943,28 +1003,29 @@ hipError_t launch_generic(const GemmArgs& a, int cfg, int64_t grid, int band) {
 
 hipError_t launch_generic_grouped(const GemmArgs& a, int cfg, int64_t grid, const int* offsets, int E) {
   switch (cfg) {
-#define X(id, bm, bn, wm, wn, st, sch) \
-  case id: return launch_generic_t<bm, bn, wm, wn, st, sch, 1>(a, grid, 0, offsets, E);
+#define X(id, bm, bn, wm, wn, st, sch, mid) \
+  case id:                              \
+    if constexpr (id < kNumGroupedGenericCfgs) return launch_generic_t<bm, bn, wm, wn, st, sch, mid, 1>(a, grid, 0, offsets, E);
     FBG_GENERIC_CFGS(X)
 #undef X
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int NB16, int MB16, int KW, int GPW, int KFIX>
+template <int NB16, int MB16, int KW, int GPW, int KFIX, int ONE>
 static hipError_t launch_skinny_t(const GemmArgs& a, int64_t grid, int S, float* ws, unsigned* cnt) {
   const dim3 blk(64 * KW);
   switch (a.out) {
     case kOutBF16:
-      hipLaunchKernelGGL((k_skinny<NB16, MB16, KW, GPW, KFIX, kOutBF16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+      hipLaunchKernelGGL((k_skinny<NB16, MB16, KW, GPW, KFIX, ONE, kOutBF16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
                          a.B, a.b_s, a.C, a.M, a.N, a.K, S, ws, cnt, a.vec);
       break;
     case kOutFP16:
-      hipLaunchKernelGGL((k_skinny<NB16, MB16, KW, GPW, KFIX, kOutFP16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+      hipLaunchKernelGGL((k_skinny<NB16, MB16, KW, GPW, KFIX, ONE, kOutFP16>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
                          a.B, a.b_s, a.C, a.M, a.N, a.K, S, ws, cnt, a.vec);
       break;
     default:
-      hipLaunchKernelGGL((k_skinny<NB16, MB16, KW, GPW, KFIX, kOutFP32>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
+      hipLaunchKernelGGL((k_skinny<NB16, MB16, KW, GPW, KFIX, ONE, kOutFP32>), dim3(grid), blk, 0, a.stream, a.A, a.a_s,
                          a.B, a.b_s, a.C, a.M, a.N, a.K, S, ws, cnt, a.vec);
   }
   return hipGetLastError();
@@ -972,8 +1033,8 @@ static hipError_t launch_skinny_t(const GemmArgs& a, int64_t grid, int S, float*
 
 hipError_t launch_swap(const GemmArgs& a, int cfg, int64_t grid, int S, float* ws, unsigned* counters) {
   switch (cfg) {
-#define X(id, nb, mb, kw, gpw) \
-  case id: return launch_skinny_t<nb, mb, kw, gpw, 0>(a, grid, S, ws, counters);
+#define X(id, nb, mb, kw, gpw, one) \
+  case id: return launch_skinny_t<nb, mb, kw, gpw, 0, one>(a, grid, S, ws, counters);
     FBG_SWAP_CFGS(X)
 #undef X
     default: return hipErrorInvalidValue;
@@ -983,7 +1044,7 @@ hipError_t launch_swap(const GemmArgs& a, int cfg, int64_t grid, int S, float* w
 hipError_t launch_short_k256(const GemmArgs& a, int cfg, int64_t grid) {
   switch (cfg) {
 #define X(id, nb, mb, kw, gpw) \
-  case id: return launch_skinny_t<nb, mb, kw, gpw, 2>(a, grid, 1, nullptr, nullptr);
+  case id: return launch_skinny_t<nb, mb, kw, gpw, 2, 0>(a, grid, 1, nullptr, nullptr);
     FBG_SHORT_CFGS(X)
 #undef X
     default: return hipErrorInvalidValue;

@@ -50,14 +50,34 @@ int64_t skinny_tiles(const SkinnyCfg& c, int64_t M, int64_t N) {
 // 5.74 us in 4 splits, 6.83 us unsplit; N = 512, M = 128, one workgroup per
 // CU unsplit: 6.79 us against 6.89 us in 2; the benchmark's back-to-back
 // replays over inputs rotated past the MALL).
+//
+// Long K (17-32 groups) with a 16 x 16 grid of at most one workgroup per CU:
+// the single-stage tile (config 22: 8 waves x 4 groups, the workgroup's whole
+// K range -- up to 128 KB -- in flight at once, one wait), unsplit.  Measured
+// (K = 4096, cold): N = 512, M = 64: 5.67 us against 6.15 us for 16 x 16 in
+// 4 splits; M = 128: 5.69 against 6.79 unsplit; N = 4096, M = 16: 6.93
+// against 7.78.  Where that grid fills at most a quarter of the device and
+// a workspace is available, splitting K over more workgroups still wins
+// (N = 512, M = 16: 5.31 us in 4 splits against 5.77); a single token keeps
+// the 8-wave register tile (config 11) unless its grid is that small
+// (N = 4096, M = 1: 5.53 against 6.07; N = 512: 4.68 with config 22 against
+// 4.92).
 struct SwapPick {
   int cfg;
   int64_t S;
 };
 
-bool swap_pick(int64_t M, int64_t N, int64_t G, int cu, SwapPick* out) {
+bool swap_pick(int64_t M, int64_t N, int64_t G, int cu, bool allow_split, SwapPick* out) {
   const int64_t W2 = cdiv(N, 16) * cdiv(M, 16), W7 = cdiv(N, 32) * cdiv(M, 16), W19 = cdiv(N, 32) * cdiv(M, 64);
   int64_t W;
+  if (G > 16 && G <= 32 && W2 <= (int64_t)cu) {
+    const bool small = 4 * W2 <= (int64_t)cu;
+    if (M <= 4 ? small : !(small && allow_split)) {
+      out->cfg = 22;
+      out->S = 1;
+      return true;
+    }
+  }
   if (W2 <= 3 * (int64_t)cu) {
     out->cfg = 2;
     W = W2;
@@ -78,7 +98,7 @@ bool swap_pick(int64_t M, int64_t N, int64_t G, int cu, SwapPick* out) {
     out->cfg = 11;
     return true;
   }
-  if (G >= 16 && M > 1 && 4 * W <= 3 * (int64_t)cu) {
+  if (allow_split && G >= 16 && M > 1 && 4 * W <= 3 * (int64_t)cu) {
     const int64_t cap = G / kSwapCfgs[out->cfg].kw < 4 ? G / kSwapCfgs[out->cfg].kw : 4;
     const int64_t want = cdiv(2 * (int64_t)cu, W);
     out->S = want < cap ? want : cap;
@@ -101,7 +121,7 @@ int64_t swap_split(const SkinnyCfg& k, int64_t tiles, int64_t G, int cu) {
 // every CU a workgroup, else 32 n x 16 m (config 7).
 int swap_cfg_for(int64_t M, int64_t N, int64_t G, int cu) {
   SwapPick p;
-  if (swap_pick(M, N, G, cu, &p)) return p.cfg;
+  if (swap_pick(M, N, G, cu, true, &p)) return p.cfg;
   if (M > 16 && cdiv(N, 32) * cdiv(M, 64) >= (int64_t)cu) return 4;
   return 7;
 }
@@ -154,7 +174,10 @@ int generic_cfg_for(int64_t M, int64_t N, int64_t G, int cu) {
     }
     if (better) best = c;
   }
-  return best;
+  // The 256 x 256 tile with its refill split at mid-group (configuration 8):
+  // prefill 16384 x 4096 x 4096 in 276 against 288 us (bf16), 294 against
+  // 305 us (fp32), interleaved runs on one box.
+  return best == 3 ? 8 : best;
 }
 
 }  // namespace
@@ -187,7 +210,9 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
 
   int v = variant;
   SwapPick pick{7, 1};
-  const bool picked = swap_pick(M, N, G, cu, &pick);
+  // split_k = 1 under AUTO: the best plan without a K split (no workspace).
+  const bool allow_split = !(variant == FBG_VARIANT_AUTO && split_k == 1);
+  const bool picked = swap_pick(M, N, G, cu, allow_split, &pick);
   if (v == FBG_VARIANT_AUTO) {
     // K == 256: short-K while its 16x16 grid fits, else generic.  Otherwise
     // swap-AB for M <= 16 and, up to M = 256, when swap_pick finds a tile;
@@ -276,7 +301,7 @@ int64_t workspace_bytes(const fbg_plan& p, int64_t M, int64_t N) {
 // (prefill-sized experts), its 256 x 256 tiles: 4096 tokens run in 242 us
 // against 275 us in 128 x 256 (a second row tile re-reads the weight) and
 // 353-511 us in every other tile.
-int grouped_num_cfgs() { return kNumGroupedCfgs + kNumGenericCfgs; }
+int grouped_num_cfgs() { return kNumGroupedCfgs + kNumGroupedGenericCfgs; }
 int grouped_num_skinny_cfgs() { return kNumGroupedCfgs; }
 
 int grouped_cfg_for(int64_t M, int64_t E, int64_t N, int64_t K, int force_cfg) {

@@ -45,9 +45,13 @@ def test_status_strings():
 def test_plan_for_the_workloads():
     p = fbg.plan(16, 512, 256)
     assert p["variant_name"] == "short_k256" and p["split_k"] == 1
+    # decode: the single-stage 16x16 tile, unsplit, one workgroup per CU
     p = fbg.plan(64, 512, 4096)
+    assert (p["variant_name"], p["config"], p["split_k"], p["grid"]) == ("swap_ab", 22, 1, 128)
+    # a grid of at most a quarter of the device splits K (with a workspace)
+    p = fbg.plan(16, 512, 4096)
     assert p["variant_name"] == "swap_ab_splitk" and p["split_k"] > 1 and p["workspace_bytes"] > 0
-    assert p["grid"] >= 256
+    assert fbg.plan(16, 512, 4096, split_k=1)["config"] == 22
     # K = 256: short-K while its 16x16 grid fits three workgroups per CU, the
     # generic kernel beyond (measured faster there)
     assert fbg.plan(32, 4096, 256)["variant_name"] == "short_k256"
@@ -61,17 +65,20 @@ def test_plan_for_the_workloads():
     # swap-AB tiles (their fragments staged through LDS) up to three 16x16 or
     # two 32x16 workgroups per CU, the generic kernel past that (the measured
     # dispatch sweep); decode splits K for two workgroups per CU, at most 4
-    p = fbg.plan(64, 512, 4096)
+    p = fbg.plan(16, 512, 4096)
     assert (p["config"], p["split_k"]) == (2, 4)
     p = fbg.plan(128, 512, 4096)
-    assert p["variant_name"] == "swap_ab" and p["config"] == 2 and p["split_k"] == 1
+    assert p["variant_name"] == "swap_ab" and p["config"] == 22 and p["split_k"] == 1
+    assert fbg.plan(1, 4096, 4096)["config"] == 11 and fbg.plan(1, 512, 4096)["config"] == 22
+    assert fbg.plan(128, 512, 1024)["config"] == 2
     p = fbg.plan(512, 512, 4096)
     assert p["variant_name"] == "swap_ab" and p["config"] == 7
     assert fbg.plan(128, 1536, 4096)["variant_name"] == "swap_ab"
     assert fbg.plan(256, 1536, 4096)["variant_name"] == "generic"
     assert fbg.plan(64, 8192, 4096)["variant_name"] == "generic"
     p = fbg.plan(16384, 4096, 4096)
-    assert p["variant_name"] == "generic" and p["workspace_bytes"] == 0
+    assert p["variant_name"] == "generic" and p["workspace_bytes"] == 0 and p["config"] == 8
+    assert (p["tile_m"], p["tile_n"], p["grid"]) == (256, 256, 1024)
 
 
 @pytest.mark.parametrize("cu", [1, 8, 80, 256, 304, 1024])
@@ -202,7 +209,8 @@ def test_every_tile_configuration_has_parity_cases():
     grouped = {c[0] for c in GROUPED_CASES}
     n_skinny = len(ids("FBG_GROUPED_CFGS"))
     assert ids("FBG_GROUPED_CFGS") <= grouped
-    assert {n_skinny + c for c in ids("FBG_GENERIC_CFGS")} <= grouped     # the generic kernel in grouped mode
+    # the generic kernel in grouped mode: configurations 0-7 (8 is dense-only)
+    assert {n_skinny + c for c in ids("FBG_GENERIC_CFGS") if c < 8} <= grouped
 
 
 def _qcall(x=0x100000, M=4, K=256, A=0x200000, a_s=0x300000):

@@ -43,6 +43,14 @@ TOL_CASES = [
     ("generic", 6, 130, 300, 1024, 0),
     ("generic", 6, 64, 33, 256, 0),
     ("generic", 6, 129, 260, 640, 0),
+    ("generic", 3, 130, 600, 1152, 0),
+    # 256x256 with the mid-group refill: several chunks of row scales, ragged
+    # tiles, fewer groups than the ring's prologue, odd group counts
+    ("generic", 8, 300, 520, 3200, 0),
+    ("generic", 8, 513, 257, 256, 0),
+    ("generic", 8, 257, 300, 2048, 0),
+    ("generic", 8, 130, 600, 1152, 0),
+    ("generic", 8, 300, 520, 640, 0),
     # 128x256 tile with 8 waves (grouped mid-size experts; forced here dense)
     ("generic", 7, 300, 520, 1024, 0),
     ("generic", 7, 129, 257, 384, 0),
@@ -101,6 +109,14 @@ TOL_CASES = [
     ("swap_ab_splitk", 10, 64, 512, 4096, 2),
     ("swap_ab_splitk", 12, 128, 256, 1024, 2),
     ("swap_ab_splitk", 14, 64, 512, 4096, 4),
+    # single-stage LDS tile: one chunk covering the range, several chunks (a
+    # wave reloading its one area), partial chunks, and splits
+    ("swap_ab", 22, 33, 260, 4096, 0),
+    ("swap_ab", 22, 64, 300, 4096, 0),
+    ("swap_ab", 22, 9, 200, 8192, 0),
+    ("swap_ab", 22, 5, 130, 1280, 0),
+    ("swap_ab_splitk", 22, 64, 512, 4096, 2),
+    ("swap_ab_splitk", 22, 40, 260, 3072, 3),
 ]
 
 
@@ -119,6 +135,8 @@ EXACT_CASES = [
     ("generic", 2, 40, 260, 512, 0),
     ("generic", 3, 260, 300, 768, 0),
     ("generic", 3, 130, 260, 4224, 0),
+    ("generic", 8, 260, 300, 768, 0),
+    ("generic", 8, 130, 260, 4224, 0),
     ("short_k256", 15, 100, 300, 256, 0),
     ("short_k256", 0, 100, 640, 256, 0),
     ("short_k256", 2, 5, 130, 256, 0),
@@ -129,6 +147,8 @@ EXACT_CASES = [
     ("swap_ab_splitk", 0, 48, 384, 1024, 2),
     ("swap_ab_splitk", 0, 48, 384, 1024, 8),
     ("swap_ab_splitk", 1, 48, 384, 1024, 3),
+    ("swap_ab", 22, 48, 384, 4096, 0),
+    ("swap_ab_splitk", 22, 48, 384, 4096, 2),
 ]
 
 
@@ -242,12 +262,12 @@ def test_concurrent_streams_with_library_workspace(gpu):
 def test_concurrent_streams_with_default_workspace(gpu):
     """The binding's default split-K workspace (a zeroed tensor from torch's
     allocator on the call's stream) on two streams at once."""
-    d1 = workloads.make_inputs(64, 512, 4096, seed=23)
-    d2 = workloads.make_inputs(16, 1536, 4096, seed=24)
+    d1 = workloads.make_inputs(32, 512, 4096, seed=23)
+    d2 = workloads.make_inputs(16, 512, 4096, seed=24)
     r1 = oracle.block_gemm(d1["A"], d1["a_s"], d1["B"], d1["b_s"])
     r2 = oracle.block_gemm(d2["A"], d2["a_s"], d2["B"], d2["b_s"])
     dd1, dd2 = to_dev(d1), to_dev(d2)
-    assert gpu.plan(64, 512, 4096)["split_k"] > 1 and gpu.plan(16, 1536, 4096)["split_k"] > 1
+    assert gpu.plan(32, 512, 4096)["split_k"] > 1 and gpu.plan(16, 512, 4096)["split_k"] > 1
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     outs = []
     for _ in range(4):
