@@ -789,11 +789,25 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
   skinny_reduce<NB16, MB16, KW>(sRed, kw, lane, acc);
 
   if (S > 1) {
-    // Publish this split's partial at device scope: agent-scope stores are
-    // written through the XCD's L2 to the device coherence point, so the
-    // reducing workgroup (maybe on another XCD) reads them without a
-    // whole-L2 writeback or invalidate.  Order: every store complete
-    // (s_waitcnt) -> barrier -> one arrival increment per workgroup.
+    // Publish this split's partial at device scope and count the arrival.
+    // The ordering contract, in the terms of the gfx950 ISA:
+    //  1. the partials are agent-scope atomic stores, which the hardware
+    //     performs write-through to the device coherence point (the memory
+    //     side of every XCD's L2), and a store leaves the wave's vmcnt only
+    //     once it is complete there;
+    //  2. every wave waits for all of its stores (s_waitcnt 0) before the
+    //     workgroup barrier, so no partial store is outstanding when
+    //  3. one wave increments the tile's counter, an agent-scope atomic
+    //     performed at the coherence point;
+    //  4. the last arrival (the increment that returns S - 1) reads the
+    //     partials with agent-scope atomic loads, served from the coherence
+    //     point and issued only after that return value reached the wave
+    //     (through the barrier), so they see every partial completed before
+    //     any earlier increment.
+    // The memory model's agent-scope release/acquire (an acq_rel increment
+    // and an acquire fence in the last arrival) gives the same order, but on
+    // gfx950 it is an L2 writeback and invalidate per workgroup: the decode
+    // shape split in 4 ran 16.8 us against 6.2 us, so it is not used.
     constexpr int TILE_ELEMS = BN * BMS;
     float* mine = ws + ((int64_t)s * T + tile) * TILE_ELEMS;
 #pragma unroll
