@@ -641,8 +641,10 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
 
 }
 
-template <int NB16, int MB16, int KW, typename Red>
-__device__ __forceinline__ void skinny_reduce(Red& sRed, int kw, int lane, v4f (&acc)[NB16][MB16]) {
+// row(q, b, r): the 64 floats of wave q's partial of block b, element r, in
+// the reduction buffer.
+template <int NB16, int MB16, int KW, typename Row>
+__device__ __forceinline__ void skinny_reduce(Row&& row, int kw, int lane, v4f (&acc)[NB16][MB16]) {
   constexpr int NBLK = NB16 * MB16;
   if constexpr (KW > 1) {
 #pragma unroll
@@ -650,21 +652,20 @@ __device__ __forceinline__ void skinny_reduce(Red& sRed, int kw, int lane, v4f (
 #pragma unroll
       for (int j = 0; j < MB16; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sRed[kw][i * MB16 + j][r][lane] = acc[i][j][r];
+        for (int r = 0; r < 4; ++r) row(kw, i * MB16 + j, r)[lane] = acc[i][j][r];
     __syncthreads();
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
       if (b % KW != kw) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float v = sRed[0][b][r][lane];
+        float v = row(0, b, r)[lane];
 #pragma unroll
-        for (int q = 1; q < KW; ++q) v += sRed[q][b][r][lane];
+        for (int q = 1; q < KW; ++q) v += row(q, b, r)[lane];
         acc[b / MB16][b % MB16][r] = v;
       }
     }
   }
-
 }
 
 // ===========================================================================
@@ -718,7 +719,11 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
   constexpr int STAGE_H = GPW * (NB16 + MB16) * 2048;  // one chunk of one wave
   constexpr int SINGLE = ONE || KFIX != 0;
   constexpr int DMA = SINGLE ? STAGE_H * KW <= 128 * 1024 : 2 * STAGE_H * KW <= 96 * 1024;
-  __shared__ __attribute__((aligned(16))) float sRed[KW > 1 ? KW : 1][NBLK][4][64];
+  // With one staging area per wave, the cross-wave sum reuses it: wave q's
+  // partials overwrite its own area once its last fragments are in registers
+  // (only that wave ever wrote or read it), so no separate buffer is needed.
+  constexpr bool RED_ALIAS = SINGLE && DMA && KW > 1 && NBLK * 1024 <= STAGE_H;
+  __shared__ __attribute__((aligned(16))) float sRed[KW > 1 && !RED_ALIAS ? KW : 1][RED_ALIAS ? 1 : NBLK][4][64];
   __shared__ __attribute__((aligned(16))) uint8_t sStage0[DMA ? STAGE_H * KW : 16];
   __shared__ __attribute__((aligned(16))) uint8_t sStage1[DMA && !SINGLE ? STAGE_H * KW : 16];
   __shared__ int sLast;
@@ -786,7 +791,12 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
                                                    sStage1 + kw * (DMA && !SINGLE ? STAGE_H : 0));
   // The KW waves' partials, summed in the fixed order kw = 0..KW-1; wave w
   // then owns blocks b with b % KW == w for the rest of the epilogue.
-  skinny_reduce<NB16, MB16, KW>(sRed, kw, lane, acc);
+  if constexpr (RED_ALIAS)
+    skinny_reduce<NB16, MB16, KW>(
+        [&](int q, int b, int r) { return reinterpret_cast<float*>(sStage0 + q * STAGE_H) + (b * 4 + r) * 64; },
+        kw, lane, acc);
+  else
+    skinny_reduce<NB16, MB16, KW>([&](int q, int b, int r) { return &sRed[q][b][r][0]; }, kw, lane, acc);
 
   if (S > 1) {
     // Publish this split's partial at device scope and count the arrival.
@@ -908,7 +918,7 @@ __device__ __forceinline__ void grouped_mtile(const uint8_t* const* pb, const fl
   skinny_tile<NB16, MBA, KW, GPW, 0>(pb, pa, pas, pbs, 0, G, kw, lane, acc);
   // The first NB16*MBA blocks of the reduction buffer, in this tile's shape.
   auto& red = *reinterpret_cast<float(*)[KW > 1 ? KW : 1][NB16 * MBA][4][64]>(&sRed[0][0][0][0]);
-  skinny_reduce<NB16, MBA, KW>(red, kw, lane, acc);
+  skinny_reduce<NB16, MBA, KW>([&](int q, int b, int r) { return &red[q][b][r][0]; }, kw, lane, acc);
   // Block (i, j): lane holds n = 16i + 4*(lane>>4) + r, m = 16j + (lane & 15).
 #pragma unroll
   for (int b = 0; b < NB16 * MBA; ++b) {

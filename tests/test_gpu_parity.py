@@ -136,6 +136,8 @@ EXACT_CASES = [
     ("generic", 3, 260, 300, 768, 0),
     ("generic", 3, 130, 260, 4224, 0),
     ("generic", 8, 260, 300, 768, 0),
+    ("generic", 4, 130, 260, 1152, 0),
+    ("generic", 6, 70, 100, 384, 0),
     ("generic", 8, 130, 260, 4224, 0),
     ("short_k256", 15, 100, 300, 256, 0),
     ("short_k256", 0, 100, 640, 256, 0),

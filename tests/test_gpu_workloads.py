@@ -5,7 +5,8 @@ Shapes drawn from the pages' trace shape sets (FlagGems-vllm PR #693, "feat:
 optimize w8a8 block fp8 matmul for Hopper", section "Performance"): the
 small, decode, short-K and mid-M shapes are compared with the oracle on every
 element (at sweep points with M >= 256 on every 8th row and the last row);
-the 16384-row prefill shape on all outlier rows plus every 64th row, and on
+the 16384-row prefill shape on all outlier rows plus every 16th row at an
+offset that walks the 16 rows of an MFMA block (16j + j mod 16), and on
 every row and column through sums that hold at any size:
   sum_n C[m,n] = sum_g a_s[m,g] sum_{k in g} A[m,k] w_g[k],  w_g[k] = sum_n b_s[n/128,g] B[n,k]
   sum_m C[m,n] = sum_g b_s[n/128,g] sum_{k in g} B[n,k] v_g[k], v_g[k] = sum_m a_s[m,g] A[m,k]
@@ -25,6 +26,13 @@ pytestmark = pytest.mark.gpu
 def _rows_sample(M, every):
     rows = np.arange(0, M, every)
     return np.unique(np.append(rows, M - 1))
+
+
+def _lane_rows(M):
+    """Every 16th row, offset so the sample walks all 16 rows of a 16-row MFMA
+    block (row 16j + j mod 16), plus the last row."""
+    j = np.arange(M // 16)
+    return np.unique(np.append(16 * j + j % 16, M - 1))
 
 
 def _check_rows(C, d, rows, out):
@@ -73,7 +81,7 @@ def test_prefill_workload(gpu):
     w = W.WORKLOADS["prefill_16384x4096x4096"]
     d = W.make_workload(w)
     dd = to_dev(d)
-    rows = np.unique(np.concatenate([d["outliers"], _rows_sample(w.M, 64)]))
+    rows = np.unique(np.concatenate([d["outliers"], _lane_rows(w.M)]))
     rsum, csum = _row_col_sums(d)
     for out in w.out_dtypes:
         C = run(gpu, dd, out)
@@ -101,7 +109,7 @@ def test_prefill_shape_exact_mode(gpu):
     out_rows = np.sort(rng.choice(M, 160, replace=False))
     d = W.make_exact_inputs(M, N, K, seed=55, u_range=(-2, 0), v_range=(-2, 0), outlier_rows=out_rows)
     C = run(gpu, to_dev(d), "fp32")
-    rows = np.unique(np.concatenate([out_rows, _rows_sample(M, 256)]))
+    rows = np.unique(np.concatenate([out_rows, _lane_rows(M)]))
     ref = oracle.block_gemm(d["A"][rows], d["a_s"][rows], d["B"], d["b_s"])
     got = C[torch.from_numpy(rows).to(C.device)].cpu().numpy().view(np.uint32)
     assert np.array_equal(got, oracle.round_bits(ref, "fp32"))
