@@ -11,9 +11,9 @@ namespace fbg {
 // per row, loaded a few rows' runs per instruction; 0: one load per row and
 // group, staged in the ring slot), mid-group refill (1: most of a group's
 // refill goes out after a second barrier in the middle of the group, spread
-// over several row blocks; the 256 x 256 tile).  Configuration 7 serves only
-// the grouped GEMM (experts of ~50-100 rows); the dense planner does not
-// consider it.  Configuration 8 (configuration 3 with the mid-group refill:
+// over several row blocks; the 256 x 256 tile).  Configuration 7 (128 x 256,
+// 8 waves) serves the grouped GEMM (experts of ~50-100 rows) and the dense
+// planner where it ties with 256 x 128.  Configuration 8 (configuration 3 with the mid-group refill:
 // the dense planner takes it wherever it would take configuration 3) serves
 // only the dense planner; the grouped GEMM offers 0-7 (the mid-group refill
 // measured slower there: the 4096-token MoE workload 259 -> 305 us).
@@ -99,7 +99,6 @@ constexpr GenericCfg kGenericCfgs[] = {
 #undef X
 };
 constexpr int kNumGenericCfgs = sizeof(kGenericCfgs) / sizeof(kGenericCfgs[0]);
-constexpr int kNumDenseGenericCfgs = 7;  // configurations the dense planner chooses from (0-6)
 constexpr int kNumGroupedGenericCfgs = 8;  // generic configurations the grouped GEMM may run (0-7)
 
 struct SkinnyCfg { int nb16, mb16, kw, gpw, one = 0; };

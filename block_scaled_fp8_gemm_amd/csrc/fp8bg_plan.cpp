@@ -126,18 +126,26 @@ int swap_cfg_for(int64_t M, int64_t N, int64_t G, int cu) {
   return 7;
 }
 
-// Short-K (K == 256, two groups): 16 n x 16 m tiles with one group per wave
-// (config 12) while their grid fits three workgroups per CU (N = 1536,
-// M = 128: 3.14 us against 3.34 us for the generic kernel); the automatic
-// dispatch sends larger shapes to the generic kernel (K = 256, N = 8192,
-// M = 512: 8.6 us against 13.0 us), and a forced short-K launch of such a
-// shape takes 32 n x 32 m (config 15) up to M = 200, 32 n x 64 m
+// Short-K (K == 256, two groups, staged through LDS): 16 n x 16 m tiles with
+// one group per wave (config 12) while their grid fits four workgroups per
+// CU, else 32 n x 16 m (config 13) while that grid fits three; the
+// automatic dispatch sends larger shapes to the generic kernel.  Measured
+// (dispatch sweep, cold): 16 x 16 at four per CU beats the generic kernel
+// (M = 32, N = 8192: 3.42 against 3.72 us; M = 64, N = 4096: 3.52 against
+// 3.77; M = 512, N = 512: 3.38 against 3.69), 32 x 16 at three per CU too
+// (M = 256, N = 1536: 3.57 against 3.78), and both lose past that (M = 128,
+// N = 4096: 3.82 at best against 3.78; M = 1024, N = 512: 3.75 against
+// 3.66; N = 8192, M = 512: 8.5 against 7.6).  A forced short-K launch of a
+// larger shape takes 32 n x 32 m (config 15) up to M = 200, 32 n x 64 m
 // (config 10) up to M = 256, else 32 n x 32 m with one wave taking both
 // groups (config 6).
-bool short_fits(int64_t M, int64_t N, int cu) { return cdiv(N, 16) * cdiv(M, 16) <= 3 * (int64_t)cu; }
+bool short_fits16(int64_t M, int64_t N, int cu) { return cdiv(N, 16) * cdiv(M, 16) <= 4 * (int64_t)cu; }
+bool short_fits32(int64_t M, int64_t N, int cu) { return cdiv(N, 32) * cdiv(M, 16) <= 3 * (int64_t)cu; }
+bool short_fits(int64_t M, int64_t N, int cu) { return short_fits16(M, N, cu) || short_fits32(M, N, cu); }
 
 int short_cfg_for(int64_t M, int64_t N, int cu) {
-  if (short_fits(M, N, cu) || M <= 48) return 12;
+  if (short_fits16(M, N, cu) || M <= 48) return 12;
+  if (short_fits32(M, N, cu)) return 13;
   if (M <= 200) return 15;
   if (M <= 256) return 10;
   return 6;
@@ -151,11 +159,18 @@ int short_cfg_for(int64_t M, int64_t N, int cu) {
 // else more waves.  For large M this is the 256 x 256 tile; in the mid-M
 // band it picks the small tiles that put a workgroup on every CU (measured:
 // M = 128, N = 8192, K = 1024 runs in 6.8 us with 64 x 64 tiles against
-// 9.3 us with 64 x 128).
+// 9.3 us with 64 x 128).  Where the 128 x 256 tile (8 waves, 3-slot ring)
+// ties with 256 x 128 (4 waves) it wins on the waves (dispatch sweep, cold:
+// M = 4096, N = 1536, K = 1024: 15.8 against 18.5 us; M = 1024, N = 8192,
+// K = 1024: 17.7 against 19.3 us; K = 4096: 45.3 against 49.1 and 50.2
+// against 50.4 us).
 int64_t generic_cost(const GenericCfg& g, int64_t M, int64_t N, int cu) {
   const int64_t wgs = cdiv(M, g.bm) * cdiv(N, g.bn);
   return cdiv(wgs, cu) * (g.bm + g.bn);
 }
+
+// The configurations the dense planner weighs (0-7; configuration 8 replaces 3).
+constexpr int kNumDenseGenericCfgs = 8;
 
 int generic_cfg_for(int64_t M, int64_t N, int64_t G, int cu) {
   int best = 0;
@@ -214,7 +229,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
   const bool allow_split = !(variant == FBG_VARIANT_AUTO && split_k == 1);
   const bool picked = swap_pick(M, N, G, cu, allow_split, &pick);
   if (v == FBG_VARIANT_AUTO) {
-    // K == 256: short-K while its 16x16 grid fits, else generic.  Otherwise
+    // K == 256: short-K while its 16x16 or 32x16 grid fits, else generic.  Otherwise
     // swap-AB for M <= 16 and, up to M = 256, when swap_pick finds a tile;
     // the generic kernel for the rest.
     if (K == 256 && M <= 1024)

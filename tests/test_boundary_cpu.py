@@ -52,11 +52,20 @@ def test_plan_for_the_workloads():
     p = fbg.plan(16, 512, 4096)
     assert p["variant_name"] == "swap_ab_splitk" and p["split_k"] > 1 and p["workspace_bytes"] > 0
     assert fbg.plan(16, 512, 4096, split_k=1)["config"] == 22
-    # K = 256: short-K while its 16x16 grid fits three workgroups per CU, the
-    # generic kernel beyond (measured faster there)
+    # K = 256: short-K while its 16x16 grid fits four workgroups per CU or its
+    # 32x16 grid three, the generic kernel beyond (measured faster there)
     assert fbg.plan(32, 4096, 256)["variant_name"] == "short_k256"
     assert fbg.plan(128, 1536, 256)["variant_name"] == "short_k256"
-    assert fbg.plan(184, 4096, 256)["variant_name"] == "generic"
+    p = fbg.plan(32, 8192, 256)
+    assert (p["variant_name"], p["config"]) == ("short_k256", 12)
+    p = fbg.plan(256, 1536, 256)
+    assert (p["variant_name"], p["config"]) == ("short_k256", 13)
+    for M in (100, 184, 214, 264):
+        assert fbg.plan(M, 4096, 256)["variant_name"] == "generic"
+    assert fbg.plan(1024, 512, 256)["variant_name"] == "generic"
+    # the 128x256 tile (8 waves) where it ties with 256x128 (4 waves)
+    assert fbg.plan(4096, 1536, 1024)["config"] == 7
+    assert fbg.plan(1024, 8192, 4096)["config"] == 7
     p = fbg.plan(128, 8192, 1024)
     assert p["variant_name"] in ("swap_ab", "swap_ab_splitk", "generic")
     # split-K only for long K with a grid of at most half the device
