@@ -550,7 +550,8 @@ def platform_floors(path, torch):
     """Launch and streaming floors of this GPU, timed like the kernels
     (HIP-graph replays, buffers rotated past the MALL, scrubbed first): a
     one-element fill (the launch-to-launch time of a kernel that does no
-    work) and device copies of 0.25 .. 256 MiB read + as many written."""
+    work), device copies of 0.25 .. 256 MiB read + as many written, and the
+    platform library's FP8 GEMM on the prefill shape."""
     lines = []
     one = [torch.empty(1, dtype=torch.float32, device="cuda:0") for _ in range(2000)]
     stream = torch.cuda.Stream()
@@ -562,10 +563,48 @@ def platform_floors(path, torch):
         us = copy_floor_us(nbytes, torch, steps=200 if mib < 64 else 20, warmup=10)
         lines.append({"floor": "copy", "read_bytes": nbytes // 2, "written_bytes": nbytes // 2,
                       "us": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    lines += library_fp8_gemm(torch)
     with open(path, "w") as f:
         for line in lines:
             f.write(json.dumps(line) + "\n")
             print(json.dumps(line), flush=True)
+
+
+def library_fp8_gemm(torch, M=16384, N=4096, K=4096, steps=20):
+    """The platform library's FP8 GEMM (hipBLASLt through torch._scaled_mm,
+    bf16 output) on the prefill shape, timed like the kernels: a reference
+    point for the MFMA-bound kernel.  It applies one scale per tensor, or one
+    per row of A and per column of B -- not the 1x128 / 128x128 block scales,
+    so it does less work than the block-scaled GEMM."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+
+    def codes(rows, cols):
+        c = torch.randint(0, 254, (rows, cols), device=dev, generator=gen, dtype=torch.int32)
+        return (c + (c >= 0x7F).int()).to(torch.uint8).view(torch.float8_e4m3fn)
+
+    copies = copies_for(M * K + N * K + 2 * M * N, 64)
+    As = [codes(M, K) for _ in range(copies)]
+    Bs = [codes(N, K) for _ in range(copies)]
+    one = torch.ones((), device=dev)
+    sa = torch.rand((M, 1), device=dev, generator=gen) + 0.5
+    sb = torch.rand((1, N), device=dev, generator=gen) + 0.5
+    stream = torch.cuda.Stream()
+    lines = []
+    for name, (x, y) in (("per tensor", (one, one)), ("per row of A and column of B", (sa, sb))):
+        def step(i):
+            torch._scaled_mm(As[i % copies], Bs[i % copies].t(), scale_a=x, scale_b=y, out_dtype=torch.bfloat16)
+
+        try:
+            ms, _ = time_steps(step, copies, steps, 5, False, stream, torch)
+        except RuntimeError as e:   # the library may not offer a scaling mode
+            lines.append({"floor": "library_fp8_gemm", "scales": name, "error": str(e)[:160]})
+            continue
+        us = ms / steps * 1e3
+        lines.append({"floor": "library_fp8_gemm", "scales": name, "M": M, "N": N, "K": K, "us": round(us, 2),
+                      "tflops": round(2 * M * N * K / us / 1e6, 1)})
+    return lines
 
 
 def copy_only(nbytes, torch, reps=5):
