@@ -176,7 +176,6 @@ int fp8bg_oracle_round(const double *x, int64_t n, int out_dtype, void *out)
     return 0;
 }
 
-/* Number of threads the OpenMP loop above uses. */
 /* ------------------------------------------------------------------------ */
 /* Per-token activation quantisation to E4M3 with one fp32 scale per row    */
 /* and 128-wide group: the producer of A and a_s (the pages' per-token      */
@@ -301,6 +300,7 @@ void fp8bg_oracle_quantize_blocks(const uint16_t *w, int64_t N, int64_t K,
     }
 }
 
+/* Number of threads the oracle's OpenMP loops use. */
 int fp8bg_oracle_threads(void)
 {
 #ifdef _OPENMP
