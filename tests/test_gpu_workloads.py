@@ -62,6 +62,24 @@ def test_workload_sweep(gpu, name, M):
     _check_rows(C, d, rows, "bf16")
 
 
+@pytest.mark.parametrize("M,N,K,variant,cfg", [
+    (32, 8192, 256, "short_k256", 12),    # 16x16 short-K tiles, four workgroups per CU
+    (256, 1536, 256, "short_k256", 13),   # 32x16 short-K tiles, three per CU
+    (4096, 1536, 1024, "generic", 7),     # 128x256 where it ties with 256x128
+    (1024, 8192, 1024, "generic", 7),
+])
+def test_dispatch_choice_at_sweep_shape(gpu, M, N, K, variant, cfg):
+    """The automatic plan at shapes of the dispatch sweep where the rules pick
+    these tiles, through fp8_block_gemm, against the oracle on every row for
+    small M and on sampled lane rows otherwise."""
+    p = gpu.plan(M, N, K)
+    assert (p["variant_name"], p["config"]) == (variant, cfg)
+    d = W.make_inputs(M, N, K, seed=71)
+    C = run(gpu, to_dev(d), "bf16")
+    rows = np.arange(M) if M <= 256 else _lane_rows(M)
+    _check_rows(C, d, rows, "bf16")
+
+
 def _row_col_sums(d):
     """fp64 row and column sums of C from O(MK + NK) work (see module doc)."""
     A, B = torch_decode(d["A"]), torch_decode(d["B"])
