@@ -631,6 +631,8 @@ def main():
     ap.add_argument("--max-copies", type=int, default=1024)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-library", action="store_true",
+                    help="skip the platform library's FP8 GEMM reference on the MFMA-bound shape")
     ap.add_argument("--sweep", default=None)
     ap.add_argument("--dispatch-sweep", default=None,
                     help="time the dispatcher's choice against every forced alternative on the pages' shape sets")
@@ -789,7 +791,15 @@ def main():
     line["copy_floor"] = {"us": round(fl, 3), "bytes": r["alg_bytes"],
                           "frac_of_floor": round(fl / (r["ms_per_step"] * 1e3), 4)}
     d = r.pop("d")
+    r_us = r["ms_per_step"]
     del r
+    if w.flops > 1e11 and not args.no_library and args.M is None:
+        # The achievable reference of an MFMA-bound shape, on the same GPU in
+        # the same run: the platform library's FP8 GEMM (no block scales).
+        lib = library_fp8_gemm(torch, w.M, w.N, w.K)
+        ref = {x["scales"]: x["us"] for x in lib if "us" in x}
+        line["achievable"] = {"library_fp8_gemm_us": ref,
+                              "frac_of_library": {k: round(v / (r_us * 1e3), 4) for k, v in ref.items()}}
     if not args.no_per_config and args.M is None and args.variant == "auto" and args.cfg is None:
         line["per_config"] = per_config(args, w.name, out, torch, fbg, W)
     if not args.no_cpu:
@@ -806,10 +816,25 @@ PER_CONFIG = [("small_16x512x256", "bf16", "ex"), ("decode_64x512x4096", "bf16",
               ("prefill_16384x4096x4096", "fp32", "ex")]
 
 
+def oracle_call_us(d, budget_s=1.0):
+    """The oracle's time for one whole GEMM of a small workload on the
+    host's cores (repeated for about `budget_s`)."""
+    import oracle
+    oracle.block_gemm(d["A"][:1], d["a_s"][:1], d["B"], d["b_s"])  # load the library
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.block_gemm(d["A"], d["a_s"], d["B"], d["b_s"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            return el / reps * 1e6
+
+
 def per_config(args, head_name, head_out, torch, fbg, W):
     """One entry per configuration of PER_CONFIG other than the headline's:
-    us per call, TFLOP/s, roofline fraction, and the fraction of a same-bytes
-    device copy.  Small shapes run 2000 steps over as many input copies (each
+    us per call, TFLOP/s, roofline fraction, the fraction of a same-bytes
+    device copy, and (small shapes) the oracle's time for the same GEMM on the
+    host's cores.  Small shapes run 2000 steps over as many input copies (each
     copy read once after the MALL scrub), the prefill shape 20."""
     res = {}
     for name, out, entry in PER_CONFIG:
@@ -822,6 +847,9 @@ def per_config(args, head_name, head_out, torch, fbg, W):
                          entry=entry, max_copies=4 if big else 2048)
         fl = copy_floor_us(r["alg_bytes"], torch)
         key = f"{name}_{out}" + ("_fp8_block_gemm" if entry != "ex" else "")
+        oracle_us = None
+        if not big and not args.no_cpu and entry == "ex":
+            oracle_us = oracle_call_us(r["d"])
         res[key] = {"M": w.M, "N": w.N, "K": w.K, "out_dtype": out, "entry": entry,
                     "variant": r["plan"]["variant_name"], "cfg": r["plan"]["config"],
                     "split_k": r["plan"]["split_k"], "grid": r["plan"]["grid"], "steps": steps,
@@ -829,6 +857,9 @@ def per_config(args, head_name, head_out, torch, fbg, W):
                     "roofline": dict(r["roof"], traffic=profiled_traffic(name, r["plan"], out)),
                     "copy_floor_us": round(fl, 3),
                     "frac_of_floor": round(fl / (r["ms_per_step"] * 1e3), 4)}
+        if oracle_us is not None:
+            res[key]["oracle_us"] = round(oracle_us, 1)
+            res[key]["gpu_speedup_over_oracle"] = round(oracle_us / (r["ms_per_step"] * 1e3), 1)
         print(f"per_config {key}: {res[key]['us']} us", file=sys.stderr, flush=True)
         del r
         torch.cuda.empty_cache()
