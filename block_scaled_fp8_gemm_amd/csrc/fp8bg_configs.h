@@ -31,9 +31,12 @@ namespace fbg {
 // Skinny kernels (swap-AB and its split-K form): id, NB16 16-row blocks of
 // weight rows (output columns n), MB16 16-column blocks of activation rows
 // (output rows m), KW waves splitting the workgroup's K range, GPW groups
-// per wave per chunk, ONE: every wave stages its chunks through a single LDS
-// area, the whole chunk's loads in flight at once (configurations whose
-// KW * GPW groups cover a launch's K range, so a wave loads once, waits once).
+// per wave per chunk, ONE: 1 -- every wave stages its chunks through a single
+// LDS area, the whole chunk's loads in flight at once (configurations whose
+// KW * GPW groups cover a launch's K range, so a wave loads once, waits
+// once); 2 -- the same with tiles of 8 activation rows (16 n x 8 m: the
+// MFMA's activation rows 8-15 are computed but never stored), which such a
+// tile never splits over K.
 #define FBG_SWAP_CFGS(X) \
   X(0, 1, 4, 4, 1, 0)    \
   X(1, 1, 4, 1, 2, 0)    \
@@ -57,7 +60,8 @@ namespace fbg {
   X(19, 2, 4, 4, 1, 0)   \
   X(20, 1, 1, 4, 4, 0)   \
   X(21, 2, 1, 4, 2, 0)   \
-  X(22, 1, 1, 8, 4, 1)
+  X(22, 1, 1, 8, 4, 1)   \
+  X(23, 1, 1, 8, 4, 2)
 
 // Short-K (K == 256, two groups, fully unrolled): same fields, KW * GPW == 2.
 #define FBG_SHORT_CFGS(X) \
@@ -124,6 +128,6 @@ constexpr SkinnyCfg kGroupedCfgs[] = {
 constexpr int kNumGroupedCfgs = sizeof(kGroupedCfgs) / sizeof(kGroupedCfgs[0]);
 
 inline int skinny_tile_n(const SkinnyCfg& c) { return 16 * c.nb16; }
-inline int skinny_tile_m(const SkinnyCfg& c) { return 16 * c.mb16; }
+inline int skinny_tile_m(const SkinnyCfg& c) { return c.one == 2 ? 8 : 16 * c.mb16; }
 
 }  // namespace fbg

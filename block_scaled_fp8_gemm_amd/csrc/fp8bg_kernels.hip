@@ -547,7 +547,11 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
 #pragma unroll
         for (int b = 0; b < NBK; ++b)
 #pragma unroll
-          for (int q = 0; q < 2; ++q) lds_dma16(rsc[b < NB16 ? 0 : 1], pd[b][q], k0, base + b * 2048 + q * 1024);
+          for (int q = 0; q < 2; ++q)
+            // ONE == 2: an activation block holds 8 rows; its rows 8-15 in
+            // LDS stay stale and feed only MFMA rows that are never stored.
+            if (ONE != 2 || b < NB16 || q == 0)
+              lds_dma16(rsc[b < NB16 ? 0 : 1], pd[b][q], k0, base + b * 2048 + q * 1024);
       } else {
 #pragma unroll
         for (int i = 0; i < NB16; ++i) ch.bf[u][i] = load_frag_global(pb[i] + k0, lane);
@@ -707,17 +711,20 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
     const float* __restrict__ b_s, void* __restrict__ C, int M, int N, int K, int S,
     float* __restrict__ ws, unsigned* __restrict__ counters, int vec_ok) {
   constexpr int BN = 16 * NB16;   // n rows per workgroup (every wave covers all of them)
-  constexpr int BMS = 16 * MB16;  // m columns per workgroup
+  constexpr bool HALF = ONE == 2;  // tiles of 8 activation rows
+  constexpr int BMS = HALF ? 8 : 16 * MB16;  // m columns per workgroup
+  constexpr int BLK_ELEMS = 16 * BN * MB16;   // FP32 partial elements of a tile (16-row blocks)
   constexpr int NBLK = NB16 * MB16;
   static_assert(128 % BN == 0, "a tile's n rows must share one b_s block");
   static_assert(KFIX == 0 || KW * GPW == KFIX, "the short-K form covers its groups in one chunk");
+  static_assert(!HALF || (MB16 == 1 && KFIX == 0), "8-row activation tiles are single 16-row blocks");
 
   // Fragments through LDS (DMA) where the staging area stays within 96 KB
   // per workgroup for two chunks per wave, or 128 KB for one (ONE, and the
   // short-K form, whose one chunk holds both groups); the other
   // configurations load straight into registers.
   constexpr int STAGE_H = GPW * (NB16 + MB16) * 2048;  // one chunk of one wave
-  constexpr int SINGLE = ONE || KFIX != 0;
+  constexpr int SINGLE = ONE != 0 || KFIX != 0;
   constexpr int DMA = SINGLE ? STAGE_H * KW <= 128 * 1024 : 2 * STAGE_H * KW <= 96 * 1024;
   // With one staging area per wave, the cross-wave sum reuses it: wave q's
   // partials overwrite its own area once its last fragments are in registers
@@ -759,7 +766,7 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
   const float* pas[MB16];
 #pragma unroll
   for (int j = 0; j < MB16; ++j) {
-    int r = m0 + 16 * j + (lane & 15);
+    int r = m0 + 16 * j + (HALF ? (lane & 7) : (lane & 15));
     r = r < M ? r : M - 1;
     pa[j] = A + (int64_t)r * ldk;
     pas[j] = a_s + (int64_t)r * G;
@@ -818,7 +825,7 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
     // and an acquire fence in the last arrival) gives the same order, but on
     // gfx950 it is an L2 writeback and invalidate per workgroup: the decode
     // shape split in 4 ran 16.8 us against 6.2 us, so it is not used.
-    constexpr int TILE_ELEMS = BN * BMS;
+    constexpr int TILE_ELEMS = BLK_ELEMS;
     float* mine = ws + ((int64_t)s * T + tile) * TILE_ELEMS;
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
@@ -877,7 +884,7 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
     const int n = n0 + 16 * i + 4 * (lane >> 4);
     const int m = m0 + 16 * j + (lane & 15);
     const int cnt = N - n < 4 ? N - n : 4;
-    if (m < M && cnt > 0) store4<OUT>(C, (int64_t)m * N + n, acc[i][j], cnt, vec_ok);
+    if ((!HALF || (lane & 15) < 8) && m < M && cnt > 0) store4<OUT>(C, (int64_t)m * N + n, acc[i][j], cnt, vec_ok);
   }
 }
 
@@ -1058,7 +1065,7 @@ static hipError_t launch_skinny_t(const GemmArgs& a, int64_t grid, int S, float*
 hipError_t launch_swap(const GemmArgs& a, int cfg, int64_t grid, int S, float* ws, unsigned* counters) {
   switch (cfg) {
 #define X(id, nb, mb, kw, gpw, one) \
-  case id: return launch_skinny_t<nb, mb, kw, gpw, 0, one>(a, grid, S, ws, counters);
+  case id: return (one == 2 && S > 1) ? hipErrorInvalidValue : launch_skinny_t<nb, mb, kw, gpw, 0, one>(a, grid, S, ws, counters);
     FBG_SWAP_CFGS(X)
 #undef X
     default: return hipErrorInvalidValue;

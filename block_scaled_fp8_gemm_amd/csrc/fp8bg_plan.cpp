@@ -51,7 +51,25 @@ int64_t skinny_tiles(const SkinnyCfg& c, int64_t M, int64_t N) {
 // CU unsplit: 6.79 us against 6.89 us in 2; the benchmark's back-to-back
 // replays over inputs rotated past the MALL).
 //
-// Long K (17-32 groups) with a 16 x 16 grid of at most one workgroup per CU:
+// 12-64 groups with a 16 n x 8 m grid of at most one workgroup per CU: the
+// single-stage tile with 8 activation rows (config 23, unsplit; a wave
+// stages 4 groups at a time, so past 32 groups it reloads its area).  A
+// single-stage workgroup's time follows its own bytes, not the grid's (K =
+// 4096, 8 waves, cold: 5.62-5.75 us at 128 KB per workgroup for 32 to 256
+// workgroups, 5.14 us at 96 KB, 4.37-4.42 us at 64 KB), and the 8-row tile
+// moves 96 KB where the 16 x 16 one moves 128: N = 512, M = 64: 4.98 us
+// against 5.64; M = 32: 4.91 against 5.75 (16 x 16 in 4 splits); M = 16:
+// 4.96 against 5.31; M = 1 and 4 (grid of at most a quarter of the device):
+// 4.40 and 4.73 against 4.63 and 4.93.  Its grid past one workgroup per CU
+// loses (N = 512, M = 128: 8.37 against 5.66), and so does a full-device
+// grid of a few tokens (N = 4096, M = 1: 5.98 against 5.56 for config 11).
+// Other K (N = 512, M = 64): 1536: 3.76 against 3.97 us; 2048: 4.05 against
+// 4.59 unsplit and 5.87 in 4 splits; 6144: 6.12 against 7.00 in 4 splits;
+// 8192: 6.96 against 7.45; 1024: 3.57 against 3.32 (not taken).  Past 32
+// groups a grid of at most a quarter of the device splits better when a
+// workspace is given (N = 512, K = 8192, M = 16: 6.47 us in 4 splits against
+// 7.08).
+// Else, with a 16 x 16 grid of at most one workgroup per CU:
 // the single-stage tile (config 22: 8 waves x 4 groups, the workgroup's whole
 // K range -- up to 128 KB -- in flight at once, one wait), unsplit.  Measured
 // (K = 4096, cold): N = 512, M = 64: 5.67 us against 6.15 us for 16 x 16 in
@@ -69,10 +87,17 @@ struct SwapPick {
 
 bool swap_pick(int64_t M, int64_t N, int64_t G, int cu, bool allow_split, SwapPick* out) {
   const int64_t W2 = cdiv(N, 16) * cdiv(M, 16), W7 = cdiv(N, 32) * cdiv(M, 16), W19 = cdiv(N, 32) * cdiv(M, 64);
+  const int64_t W23 = cdiv(N, 16) * cdiv(M, 8);
   int64_t W;
-  if (G > 16 && G <= 32 && W2 <= (int64_t)cu) {
+  if (G >= 12 && G <= 64) {
     const bool small = 4 * W2 <= (int64_t)cu;
-    if (M <= 4 ? small : !(small && allow_split)) {
+    const bool split_wins = G > 32 && M > 4 && 4 * W23 <= (int64_t)cu && allow_split;
+    if (W23 <= (int64_t)cu && (M > 4 || small) && !split_wins) {
+      out->cfg = 23;
+      out->S = 1;
+      return true;
+    }
+    if (G > 16 && G <= 32 && W2 <= (int64_t)cu && (M <= 4 ? small : !(small && allow_split))) {
       out->cfg = 22;
       out->S = 1;
       return true;
@@ -105,6 +130,17 @@ bool swap_pick(int64_t M, int64_t N, int64_t G, int cu, bool allow_split, SwapPi
     if (out->S < 1) out->S = 1;
   }
   return true;
+}
+
+// The configuration with the same tile as an 8-row one, with 16 activation
+// rows (the single-stage tile 23 -> 22).
+int sixteen_row_twin(int c) {
+  const SkinnyCfg& k = kSwapCfgs[c];
+  for (int i = 0; i < kNumSwapCfgs; ++i) {
+    const SkinnyCfg& t = kSwapCfgs[i];
+    if (t.one == 1 && t.nb16 == k.nb16 && t.mb16 == k.mb16 && t.kw == k.kw && t.gpw == k.gpw) return i;
+  }
+  return 2;
 }
 
 // Forced split-K without a split count: split until the grid covers the
@@ -263,7 +299,11 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
     out->waves = k.kw;
     out->grid = skinny_tiles(k, M, N);
   } else {  // SWAP_AB or SWAP_AB_SPLITK
-    const int c = force_cfg >= 0 ? force_cfg : (picked ? pick.cfg : swap_cfg_for(M, N, G, cu));
+    int c = force_cfg >= 0 ? force_cfg : (picked ? pick.cfg : swap_cfg_for(M, N, G, cu));
+    // A split asked for without a configuration: the 8-row tile's 16-row
+    // counterpart, whose partials the split-K workspace holds.
+    if (force_cfg < 0 && kSwapCfgs[c].one == 2 && (split_k > 1 || variant == FBG_VARIANT_SWAP_AB_SPLITK))
+      c = sixteen_row_twin(c);
     const SkinnyCfg& k = kSwapCfgs[c];
     const int64_t tiles = skinny_tiles(k, M, N);
     int64_t S = 1;
@@ -275,6 +315,9 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
     } else if (variant == FBG_VARIANT_SWAP_AB_SPLITK) {
       S = swap_split(k, tiles, G, cu);  // forced split-K: fill the device
     }
+    // Tiles of 8 activation rows keep their partials in 16-row blocks: they
+    // never split over K.
+    if (k.one == 2 && S > 1) return FBG_ERROR_UNSUPPORTED;
     if (variant == FBG_VARIANT_AUTO) v = S > 1 ? FBG_VARIANT_SWAP_AB_SPLITK : FBG_VARIANT_SWAP_AB;
     out->variant = v;
     out->config = c;

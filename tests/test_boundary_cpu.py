@@ -45,13 +45,24 @@ def test_status_strings():
 def test_plan_for_the_workloads():
     p = fbg.plan(16, 512, 256)
     assert p["variant_name"] == "short_k256" and p["split_k"] == 1
-    # decode: the single-stage 16x16 tile, unsplit, one workgroup per CU
+    # decode: the single-stage tile of 8 activation rows, unsplit, one
+    # workgroup per CU
     p = fbg.plan(64, 512, 4096)
-    assert (p["variant_name"], p["config"], p["split_k"], p["grid"]) == ("swap_ab", 22, 1, 128)
-    # a grid of at most a quarter of the device splits K (with a workspace)
-    p = fbg.plan(16, 512, 4096)
+    assert (p["variant_name"], p["config"], p["split_k"], p["grid"]) == ("swap_ab", 23, 1, 256)
+    assert fbg.plan(16, 512, 4096)["config"] == 23 and fbg.plan(16, 512, 4096)["split_k"] == 1
+    # past one workgroup per CU in 8-row tiles, the 16x16 single-stage tile
+    p = fbg.plan(128, 512, 4096)
+    assert (p["config"], p["split_k"], p["grid"]) == (22, 1, 256)
+    # K = 8192 with a grid of at most a quarter of the device splits K (with
+    # a workspace), else the 8-row tile
+    p = fbg.plan(16, 512, 8192)
     assert p["variant_name"] == "swap_ab_splitk" and p["split_k"] > 1 and p["workspace_bytes"] > 0
-    assert fbg.plan(16, 512, 4096, split_k=1)["config"] == 22
+    assert fbg.plan(16, 512, 8192, split_k=1)["config"] == 23
+    assert fbg.plan(64, 512, 8192)["config"] == 23
+    # past 64 groups the split rule alone (a grid of at most three quarters of
+    # the device)
+    p = fbg.plan(32, 512, 16384)
+    assert p["variant_name"] == "swap_ab_splitk" and p["split_k"] == 4
     # K = 256: short-K while its 16x16 grid fits four workgroups per CU or its
     # 32x16 grid three, the generic kernel beyond (measured faster there)
     assert fbg.plan(32, 4096, 256)["variant_name"] == "short_k256"
@@ -74,11 +85,10 @@ def test_plan_for_the_workloads():
     # swap-AB tiles (their fragments staged through LDS) up to three 16x16 or
     # two 32x16 workgroups per CU, the generic kernel past that (the measured
     # dispatch sweep); decode splits K for two workgroups per CU, at most 4
-    p = fbg.plan(16, 512, 4096)
+    p = fbg.plan(16, 512, 16384)
     assert (p["config"], p["split_k"]) == (2, 4)
-    p = fbg.plan(128, 512, 4096)
-    assert p["variant_name"] == "swap_ab" and p["config"] == 22 and p["split_k"] == 1
-    assert fbg.plan(1, 4096, 4096)["config"] == 11 and fbg.plan(1, 512, 4096)["config"] == 22
+    assert fbg.plan(64, 512, 1536)["config"] == 23 and fbg.plan(64, 512, 1024)["config"] != 23
+    assert fbg.plan(1, 4096, 4096)["config"] == 11 and fbg.plan(1, 512, 4096)["config"] == 23
     assert fbg.plan(128, 512, 1024)["config"] == 2
     p = fbg.plan(512, 512, 4096)
     assert p["variant_name"] == "swap_ab" and p["config"] == 7
@@ -153,6 +163,15 @@ def test_workspace_size_for_forced_split():
     p = fbg.plan(64, 512, 4096, variant="swap_ab_splitk", split_k=8)
     assert n == p["workspace_bytes"] > 0
     assert fbg.workspace_size(64, 512, 4096, "generic", 1) == 0
+
+
+def test_eight_row_tiles_never_split(monkeypatch):
+    """The swap-AB tile of 8 activation rows (configuration 23) keeps its
+    partials in 16-row blocks, so the planner refuses to split it over K."""
+    monkeypatch.setenv("FBG_FORCE_CONFIG", "23")
+    with pytest.raises(fbg.FP8BGError):
+        fbg.workspace_size(64, 512, 4096, "swap_ab_splitk", 2)
+    assert fbg.workspace_size(64, 512, 4096, "swap_ab", 1) == 0
 
 
 def _call(A=0x10000, a_s=0x20000, B=0x30000, b_s=0x40000, C=0x50000000, M=16, N=256, K=256, out=0,

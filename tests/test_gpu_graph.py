@@ -45,7 +45,7 @@ def replay_and_check(capture, eager, refill, replays=4):
 
 
 def test_split_k_gemm_with_caller_workspace_in_a_graph(gpu):
-    M, N, K = 32, 512, 4096
+    M, N, K = 32, 512, 16384
     p = fbg.plan(M, N, K)
     assert p["variant_name"] == "swap_ab_splitk"
     dd = to_dev(workloads.make_inputs(M, N, K, seed=31))
@@ -168,7 +168,7 @@ def test_plain_entry_point_in_a_graph(gpu):
 def test_split_k_gemm_with_default_workspace_in_a_graph(gpu):
     """The binding's default workspace (a zeroed torch tensor on the call's
     stream) captured into the graph's memory pool."""
-    M, N, K = 16, 512, 4096
+    M, N, K = 16, 512, 16384
     assert fbg.plan(M, N, K)["split_k"] > 1
     dd = to_dev(workloads.make_inputs(M, N, K, seed=33))
     C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)

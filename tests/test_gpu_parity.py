@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads
 from tests._cases import golden_cases
-from tests._gpu import assert_bitwise, assert_within_tolerance, bits, run, to_dev
+from tests._gpu import assert_bitwise, assert_within_tolerance, bits, forced_config, run, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -117,6 +117,15 @@ TOL_CASES = [
     ("swap_ab", 22, 5, 130, 1280, 0),
     ("swap_ab_splitk", 22, 64, 512, 4096, 2),
     ("swap_ab_splitk", 22, 40, 260, 3072, 3),
+    # the single-stage tile with 8 activation rows: ragged M (a last tile of
+    # 1-7 rows), ragged N, K of fewer groups than the tile's 32, exactly 32,
+    # and more (the single area reloaded)
+    ("swap_ab", 23, 64, 512, 4096, 0),
+    ("swap_ab", 23, 5, 130, 1280, 0),
+    ("swap_ab", 23, 70, 300, 2048, 0),
+    ("swap_ab", 23, 9, 200, 8192, 0),
+    ("swap_ab", 23, 13, 260, 384, 0),
+    ("swap_ab", 23, 1, 40, 4096, 0),
 ]
 
 
@@ -151,6 +160,8 @@ EXACT_CASES = [
     ("swap_ab_splitk", 1, 48, 384, 1024, 3),
     ("swap_ab", 22, 48, 384, 4096, 0),
     ("swap_ab_splitk", 22, 48, 384, 4096, 2),
+    ("swap_ab", 23, 48, 384, 4096, 0),
+    ("swap_ab", 23, 13, 130, 2560, 0),
 ]
 
 
@@ -264,12 +275,12 @@ def test_concurrent_streams_with_library_workspace(gpu):
 def test_concurrent_streams_with_default_workspace(gpu):
     """The binding's default split-K workspace (a zeroed tensor from torch's
     allocator on the call's stream) on two streams at once."""
-    d1 = workloads.make_inputs(32, 512, 4096, seed=23)
-    d2 = workloads.make_inputs(16, 512, 4096, seed=24)
+    d1 = workloads.make_inputs(32, 512, 16384, seed=23)
+    d2 = workloads.make_inputs(16, 512, 16384, seed=24)
     r1 = oracle.block_gemm(d1["A"], d1["a_s"], d1["B"], d1["b_s"])
     r2 = oracle.block_gemm(d2["A"], d2["a_s"], d2["B"], d2["b_s"])
     dd1, dd2 = to_dev(d1), to_dev(d2)
-    assert gpu.plan(32, 512, 4096)["split_k"] > 1 and gpu.plan(16, 512, 4096)["split_k"] > 1
+    assert gpu.plan(32, 512, 16384)["split_k"] > 1 and gpu.plan(16, 512, 16384)["split_k"] > 1
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     outs = []
     for _ in range(4):
@@ -349,6 +360,9 @@ def test_error_statuses(gpu):
     with pytest.raises(gpu.FP8BGError) as e:
         gpu.gemm(d["A"], d["a_s"], d["B"], d["b_s"], variant="swap_ab_splitk", split_k=5)
     assert e.value.status == gpu.UNSUPPORTED       # S > K/128
+    with forced_config(23), pytest.raises(gpu.FP8BGError) as e:   # 8-row tiles never split
+        gpu.gemm(d["A"], d["a_s"], d["B"], d["b_s"], variant="swap_ab_splitk", split_k=2)
+    assert e.value.status == gpu.UNSUPPORTED
     ws = torch.zeros(16, dtype=torch.uint8, device="cuda:0")
     with pytest.raises(gpu.FP8BGError) as e:
         gpu.gemm(d["A"], d["a_s"], d["B"], d["b_s"], variant="swap_ab_splitk", split_k=4, workspace=ws)

@@ -23,7 +23,7 @@ def shapes():
     while len(out) < 48:
         M = int(rng.choice([rng.integers(1, 33), rng.integers(33, 300), rng.integers(300, 1100)]))
         N = int(rng.choice([rng.integers(1, 200), rng.integers(200, 1200), rng.integers(1200, 2600)]))
-        K = int(128 * rng.choice([1, 2, 2, 3, 8, 16, 24]))
+        K = int(128 * rng.choice([1, 2, 2, 3, 8, 16, 24, 96]))
         if M * N * K <= 3e8:
             out.append((M, N, K))
     return out

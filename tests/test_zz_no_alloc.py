@@ -24,8 +24,8 @@ def test_noalloc_matches_the_workspace_entry_point(gpu):
     # a decode shape the dispatcher splits in four, then a smaller one that
     # also splits, then a forced split of a ragged shape: each call's output
     # equals fp8_block_gemm_ex's with a caller workspace, bit for bit
-    cases = [((32, 512, 4096), "auto", 0, torch.bfloat16),
-             ((16, 512, 4096), "auto", 0, torch.bfloat16),
+    cases = [((32, 512, 16384), "auto", 0, torch.bfloat16),
+             ((16, 512, 16384), "auto", 0, torch.bfloat16),
              ((50, 300, 2048), "swap_ab_splitk", 3, torch.float32)]
     for (M, N, K), variant, split_k, od in cases:
         p = gpu.plan(M, N, K, od, torch.cuda.get_device_properties(0).multi_processor_count, variant, split_k)
@@ -44,7 +44,7 @@ def test_noalloc_matches_the_workspace_entry_point(gpu):
 def test_noalloc_repeated_calls_on_a_stream(gpu):
     # calls ordered on one stream reuse the scratch: each leaves the counters
     # zero for the next (a wrong count would make a tile skip its reduction)
-    M, N, K = 32, 512, 4096
+    M, N, K = 32, 512, 16384
     d = workloads.make_inputs(M, N, K, seed=5)
     dd = to_dev(d)
     want = _ex(gpu, dd, M, N, K, torch.bfloat16)
