@@ -14,9 +14,12 @@ namespace fbg {
 // over several row blocks; the 256 x 256 tile).  Configuration 7 (128 x 256,
 // 8 waves) serves the grouped GEMM (experts of ~50-100 rows) and the dense
 // planner where it ties with 256 x 128.  Configuration 8 (configuration 3 with the mid-group refill:
-// the dense planner takes it wherever it would take configuration 3) serves
-// only the dense planner; the grouped GEMM offers 0-7 (the mid-group refill
-// measured slower there: the 4096-token MoE workload 259 -> 305 us).
+// the dense planner takes it wherever it would take configuration 3) and 9
+// (configuration 4's 64 x 64 tile with 2 x 2 waves of 32 x 32, so all four
+// SIMDs run MFMAs; the dense planner takes it wherever it would take
+// configuration 4) serve only the dense planner; the grouped GEMM offers 0-7
+// (the mid-group refill measured slower there: the 4096-token MoE workload
+// 259 -> 305 us).
 #define FBG_GENERIC_CFGS(X)     \
   X(0, 128, 128, 2, 2, 4, 0, 0) \
   X(1, 256, 128, 2, 2, 3, 0, 0) \
@@ -26,7 +29,8 @@ namespace fbg {
   X(5, 128, 64, 2, 2, 3, 0, 0)  \
   X(6, 64, 32, 1, 2, 4, 0, 0)   \
   X(7, 128, 256, 2, 4, 3, 0, 0) \
-  X(8, 256, 256, 2, 4, 2, 1, 1)
+  X(8, 256, 256, 2, 4, 2, 1, 1) \
+  X(9, 64, 64, 2, 2, 4, 0, 0)
 
 // Skinny kernels (swap-AB and its split-K form): id, NB16 16-row blocks of
 // weight rows (output columns n), MB16 16-column blocks of activation rows

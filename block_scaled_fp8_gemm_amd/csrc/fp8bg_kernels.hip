@@ -116,7 +116,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one b_s block");
   static_assert(BM % 64 == 0 && (!SCH || RF == 1 || RF == 2) && CH % RF == 0, "a chunk's images must split evenly over the waves");
   static_assert(CH * IB <= 64 && 64 % (CH * IB) == 0, "a load image holds whole row classes");
-  static_assert(SCH || IB == 4 || IB == 8, "a lane reads its row scales of a slot as one or two 16-byte words");
+  static_assert(SCH || IB == 2 || IB == 4 || IB == 8, "a lane reads its row scales of a slot as 8 or 16-byte words");
   static_assert(STAGES >= 2 && STAGES <= 8 && LDS_CU / (RING_BYTES + 3 * CB_BYTES) >= PER_CU, "LDS ring must fit in 160 KB");
   static_assert((STAGES - 1) * LPG + CH / RF < 64, "vmcnt counts at most 63 outstanding loads");
   // MID = 1: a group's refill is split at a second barrier in the middle of
@@ -311,12 +311,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 #pragma unroll
       for (int i = 0; i < IB; ++i) as_o[i] = cs[CH * i];
     } else {
-      const v4f* ps = reinterpret_cast<const v4f*>(base + A_BYTES + B_BYTES + 64 * 4) + (wm * 16 + (lane & 15)) * IB / 4;
+      if constexpr (IB >= 4) {
+        const v4f* ps = reinterpret_cast<const v4f*>(base + A_BYTES + B_BYTES + 64 * 4) + (wm * 16 + (lane & 15)) * IB / 4;
 #pragma unroll
-      for (int q = 0; q < IB / 4; ++q) {
-        const v4f v = ps[q];
+        for (int q = 0; q < IB / 4; ++q) {
+          const v4f v = ps[q];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) as_o[4 * q + r] = v[r];
+          for (int r = 0; r < 4; ++r) as_o[4 * q + r] = v[r];
+        }
+      } else {  // two row blocks per wave: the lane's two scales as one 8-byte word
+        typedef float v2f __attribute__((ext_vector_type(2)));
+        const v2f v = reinterpret_cast<const v2f*>(base + A_BYTES + B_BYTES + 64 * 4)[wm * 16 + (lane & 15)];
+        as_o[0] = v[0];
+        as_o[1] = v[1];
       }
     }
     af_o = load_frag_lds_sw(base, wm * WM, lane);
@@ -510,7 +517,7 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
                                             const float* const* pas, const float* pbs, int g_lo, int g_hi, int kw,
                                             int lane, v4f (&acc)[NB16][MB16],
                                             const uint32_t (*pd)[2] = nullptr, const buf_rsrc* rsc = nullptr, uint8_t* stage0 = nullptr,
-                                            uint8_t* stage1 = nullptr) {
+                                            uint8_t* stage1 = nullptr, int arows = 8) {
   struct Chunk {
     v8i bf[GPW][NB16];
     v8i af[GPW][MB16];
@@ -547,11 +554,16 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
 #pragma unroll
         for (int b = 0; b < NBK; ++b)
 #pragma unroll
-          for (int q = 0; q < 2; ++q)
-            // ONE == 2: an activation block holds 8 rows; its rows 8-15 in
+          for (int q = 0; q < 2; ++q) {
+            // ONE == 2: an activation block holds 8 rows, of which the lanes
+            // of the tile's arows real rows load theirs; the other rows in
             // LDS stay stale and feed only MFMA rows that are never stored.
-            if (ONE != 2 || b < NB16 || q == 0)
+            if (ONE == 2 && b >= NB16) {
+              if (q == 0 && (lane >> 3) < arows) lds_dma16(rsc[1], pd[b][0], k0, base + b * 2048);
+            } else {
               lds_dma16(rsc[b < NB16 ? 0 : 1], pd[b][q], k0, base + b * 2048 + q * 1024);
+            }
+          }
       } else {
 #pragma unroll
         for (int i = 0; i < NB16; ++i) ch.bf[u][i] = load_frag_global(pb[i] + k0, lane);
@@ -795,7 +807,8 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
   v4f acc[NB16][MB16];
   skinny_tile<NB16, MB16, KW, GPW, KFIX, DMA, ONE>(pb, pa, pas, pbs, g_lo, g_hi, kw, lane, acc, pd, rsc,
                                                    sStage0 + kw * (DMA ? STAGE_H : 0),
-                                                   sStage1 + kw * (DMA && !SINGLE ? STAGE_H : 0));
+                                                   sStage1 + kw * (DMA && !SINGLE ? STAGE_H : 0),
+                                                   M - m0 < 8 ? M - m0 : 8);
   // The KW waves' partials, summed in the fixed order kw = 0..KW-1; wave w
   // then owns blocks b with b % KW == w for the rest of the epilogue.
   if constexpr (RED_ALIAS)

@@ -59,10 +59,12 @@ int64_t skinny_tiles(const SkinnyCfg& c, int64_t M, int64_t N) {
 // workgroups, 5.14 us at 96 KB, 4.37-4.42 us at 64 KB), and the 8-row tile
 // moves 96 KB where the 16 x 16 one moves 128: N = 512, M = 64: 4.98 us
 // against 5.64; M = 32: 4.91 against 5.75 (16 x 16 in 4 splits); M = 16:
-// 4.96 against 5.31; M = 1 and 4 (grid of at most a quarter of the device):
-// 4.40 and 4.73 against 4.63 and 4.93.  Its grid past one workgroup per CU
-// loses (N = 512, M = 128: 8.37 against 5.66), and so does a full-device
-// grid of a few tokens (N = 4096, M = 1: 5.98 against 5.56 for config 11).
+// 4.96 against 5.31.  Up to 4 tokens it needs a grid of at most half the
+// device (N = 512, M = 1 and 4: 4.40 and 4.73 against 4.63 and 4.93; N =
+// 1536: 4.66 and 4.98 against 5.03 and 5.72 for config 11); a full-device
+// grid of a few tokens loses (N = 4096, M = 1: 5.97 against 5.57 for config
+// 11), and so does a grid past one workgroup per CU (N = 512, M = 128: 8.37
+// against 5.66).
 // Other K (N = 512, M = 64): 1536: 3.76 against 3.97 us; 2048: 4.05 against
 // 4.59 unsplit and 5.87 in 4 splits; 6144: 6.12 against 7.00 in 4 splits;
 // 8192: 6.96 against 7.45; 1024: 3.57 against 3.32 (not taken).  Past 32
@@ -92,7 +94,7 @@ bool swap_pick(int64_t M, int64_t N, int64_t G, int cu, bool allow_split, SwapPi
   if (G >= 12 && G <= 64) {
     const bool small = 4 * W2 <= (int64_t)cu;
     const bool split_wins = G > 32 && M > 4 && 4 * W23 <= (int64_t)cu && allow_split;
-    if (W23 <= (int64_t)cu && (M > 4 || small) && !split_wins) {
+    if (W23 <= (int64_t)cu && (M > 4 || 2 * W23 <= (int64_t)cu) && !split_wins) {
       out->cfg = 23;
       out->S = 1;
       return true;
@@ -205,7 +207,8 @@ int64_t generic_cost(const GenericCfg& g, int64_t M, int64_t N, int cu) {
   return cdiv(wgs, cu) * (g.bm + g.bn);
 }
 
-// The configurations the dense planner weighs (0-7; configuration 8 replaces 3).
+// The configurations the dense planner weighs (0-7; configuration 8 replaces
+// 3, configuration 9 replaces 4).
 constexpr int kNumDenseGenericCfgs = 8;
 
 int generic_cfg_for(int64_t M, int64_t N, int64_t G, int cu) {
@@ -227,8 +230,12 @@ int generic_cfg_for(int64_t M, int64_t N, int64_t G, int cu) {
   }
   // The 256 x 256 tile with its refill split at mid-group (configuration 8):
   // prefill 16384 x 4096 x 4096 in 276 against 288 us (bf16), 294 against
-  // 305 us (fp32), interleaved runs on one box.
-  return best == 3 ? 8 : best;
+  // 305 us (fp32), interleaved runs on one box.  The 64 x 64 tile with 2 x 2
+  // waves (configuration 9) where the 2-wave one wins the cost: 1.6-3.9%
+  // faster at every such shape of the dispatch sweep (cold: 128 x 8192 x
+  // 1024 6.22 against 6.42 us; 184 x 4096 x 256 3.93 against 4.06; 512 x
+  // 1536 x 4096 14.56 against 15.15; 256 x 4096 x 1024 5.99 against 6.24).
+  return best == 3 ? 8 : (best == 4 ? 9 : best);
 }
 
 }  // namespace

@@ -89,6 +89,7 @@ def test_plan_for_the_workloads():
     assert (p["config"], p["split_k"]) == (2, 4)
     assert fbg.plan(64, 512, 1536)["config"] == 23 and fbg.plan(64, 512, 1024)["config"] != 23
     assert fbg.plan(1, 4096, 4096)["config"] == 11 and fbg.plan(1, 512, 4096)["config"] == 23
+    assert fbg.plan(4, 1536, 4096)["config"] == 23 and fbg.plan(4, 4096, 4096)["config"] == 11
     assert fbg.plan(128, 512, 1024)["config"] == 2
     p = fbg.plan(512, 512, 4096)
     assert p["variant_name"] == "swap_ab" and p["config"] == 7

@@ -51,6 +51,12 @@ TOL_CASES = [
     ("generic", 8, 257, 300, 2048, 0),
     ("generic", 8, 130, 600, 1152, 0),
     ("generic", 8, 300, 520, 640, 0),
+    # 2x2 waves of 32x32: two row blocks per wave, ragged tiles, fewer groups
+    # than ring slots, more (slots refilled)
+    ("generic", 9, 128, 1094, 1024, 0),
+    ("generic", 9, 65, 300, 384, 0),
+    ("generic", 9, 130, 260, 2560, 0),
+    ("generic", 9, 1, 40, 256, 0),
     # 128x256 tile with 8 waves (grouped mid-size experts; forced here dense)
     ("generic", 7, 300, 520, 1024, 0),
     ("generic", 7, 129, 257, 384, 0),
@@ -146,6 +152,7 @@ EXACT_CASES = [
     ("generic", 3, 130, 260, 4224, 0),
     ("generic", 8, 260, 300, 768, 0),
     ("generic", 4, 130, 260, 1152, 0),
+    ("generic", 9, 130, 260, 1024, 0),
     ("generic", 6, 70, 100, 384, 0),
     ("generic", 8, 130, 260, 4224, 0),
     ("short_k256", 15, 100, 300, 256, 0),
