@@ -485,8 +485,9 @@ def dispatch_sweep(path, torch, fbg, steps=100, warmup=10):
                             "b_s": torch.rand((NB, G), device=dev, generator=gen) * 0.01 + 1e-3}
                     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
                     outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
-                    cands = [("auto", None)] + [("generic", c) for c in range(9)]
+                    cands = [("auto", None)] + [("generic", c) for c in range(12)]
                     cands += [(v, c) for v in ("swap_ab", "swap_ab_splitk") for c in (2, 4, 7, 12, 19, 22)]
+                    cands += [("swap_ab", 23)]   # 8-row tiles never split
                     if K == 256:
                         cands += [("short_k256", c) for c in range(16)]
                     cands += [("auto", None)]   # timed first and last: the faster of the two counts

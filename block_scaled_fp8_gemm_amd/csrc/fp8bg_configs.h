@@ -17,7 +17,9 @@ namespace fbg {
 // the dense planner takes it wherever it would take configuration 3) and 9
 // (configuration 4's 64 x 64 tile with 2 x 2 waves of 32 x 32, so all four
 // SIMDs run MFMAs; the dense planner takes it wherever it would take
-// configuration 4) serve only the dense planner; the grouped GEMM offers 0-7
+// configuration 4), 10 (configuration 2's 64 x 128 tile with 2 x 2 waves)
+// and 11 (configuration 0's 128 x 128 tile with 8 waves, taken for K of at
+// most 1024) serve only the dense planner; the grouped GEMM offers 0-7
 // (the mid-group refill measured slower there: the 4096-token MoE workload
 // 259 -> 305 us).
 #define FBG_GENERIC_CFGS(X)     \
@@ -30,7 +32,9 @@ namespace fbg {
   X(6, 64, 32, 1, 2, 4, 0, 0)   \
   X(7, 128, 256, 2, 4, 3, 0, 0) \
   X(8, 256, 256, 2, 4, 2, 1, 1) \
-  X(9, 64, 64, 2, 2, 4, 0, 0)
+  X(9, 64, 64, 2, 2, 4, 0, 0)   \
+  X(10, 64, 128, 2, 2, 4, 0, 0) \
+  X(11, 128, 128, 2, 4, 4, 0, 0)
 
 // Skinny kernels (swap-AB and its split-K form): id, NB16 16-row blocks of
 // weight rows (output columns n), MB16 16-column blocks of activation rows

@@ -207,8 +207,8 @@ int64_t generic_cost(const GenericCfg& g, int64_t M, int64_t N, int cu) {
   return cdiv(wgs, cu) * (g.bm + g.bn);
 }
 
-// The configurations the dense planner weighs (0-7; configuration 8 replaces
-// 3, configuration 9 replaces 4).
+// The configurations the dense planner weighs (0-7; configurations 8-11
+// replace 3, 4, 2 and 0 where they measured faster).
 constexpr int kNumDenseGenericCfgs = 8;
 
 int generic_cfg_for(int64_t M, int64_t N, int64_t G, int cu) {
@@ -235,7 +235,17 @@ int generic_cfg_for(int64_t M, int64_t N, int64_t G, int cu) {
   // faster at every such shape of the dispatch sweep (cold: 128 x 8192 x
   // 1024 6.22 against 6.42 us; 184 x 4096 x 256 3.93 against 4.06; 512 x
   // 1536 x 4096 14.56 against 15.15; 256 x 4096 x 1024 5.99 against 6.24).
-  return best == 3 ? 8 : (best == 4 ? 9 : best);
+  // The 64 x 128 tile with 2 x 2 waves (configuration 10) where the 2-wave
+  // one wins: 4-7% faster at every such shape (K = 4096: 1024 x 1536 20.6
+  // against 22.0 us; 512 x 4096 21.7 against 23.0; 4096 x 512 21.4 against
+  // 22.9).  The 128 x 128 tile with 8 waves (configuration 11) for K of at
+  // most 1024 (1024 x 4096 x 256 7.09 against 7.53 us; 512 x 8192 x 1024
+  // 11.58 against 11.98); at K = 4096 it loses (33.4 against 30.5 us).
+  if (best == 3) return 8;
+  if (best == 4) return 9;
+  if (best == 2) return 10;
+  if (best == 0 && G <= 8) return 11;
+  return best;
 }
 
 }  // namespace

@@ -57,6 +57,10 @@ TOL_CASES = [
     ("generic", 9, 65, 300, 384, 0),
     ("generic", 9, 130, 260, 2560, 0),
     ("generic", 9, 1, 40, 256, 0),
+    ("generic", 10, 130, 300, 1024, 0),
+    ("generic", 10, 64, 130, 384, 0),
+    ("generic", 11, 300, 260, 1024, 0),
+    ("generic", 11, 129, 257, 384, 0),
     # 128x256 tile with 8 waves (grouped mid-size experts; forced here dense)
     ("generic", 7, 300, 520, 1024, 0),
     ("generic", 7, 129, 257, 384, 0),
