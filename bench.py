@@ -788,6 +788,10 @@ def main():
         # The plan call reports the automatic tile; a forced configuration's
         # tile and grid are not known here.
         line["config"].update(forced_cfg=args.cfg, tile=None, grid=None)
+    props = torch.cuda.get_device_properties(0)
+    line["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                      "compute_units": props.multi_processor_count,
+                      "memory_gib": round(props.total_memory / 2**30, 1)}
     fl = copy_floor_us(r["alg_bytes"], torch)
     line["copy_floor"] = {"us": round(fl, 3), "bytes": r["alg_bytes"],
                           "frac_of_floor": round(fl / (r["ms_per_step"] * 1e3), 4)}
