@@ -149,6 +149,11 @@ __device__ __forceinline__ buf_rsrc make_rsrc_n(const void* base, uint32_t bytes
 __device__ __forceinline__ void lds_dma16(buf_rsrc r, uint32_t voff, int soff, lds_u8* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voff, soff, 0, 0);
 }
+// The same with the non-temporal hint, for bytes that one workgroup reads
+// once and no later workgroup reads again.
+__device__ __forceinline__ void lds_dma16_nt(buf_rsrc r, uint32_t voff, int soff, lds_u8* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voff, soff, 0, 2);
+}
 __device__ __forceinline__ void lds_dma4(buf_rsrc r, uint32_t voff, int soff, lds_u8* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, (int)voff, soff, 0, 0);
 }

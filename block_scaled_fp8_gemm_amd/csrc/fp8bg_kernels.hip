@@ -517,7 +517,8 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
                                             const float* const* pas, const float* pbs, int g_lo, int g_hi, int kw,
                                             int lane, v4f (&acc)[NB16][MB16],
                                             const uint32_t (*pd)[2] = nullptr, const buf_rsrc* rsc = nullptr, uint8_t* stage0 = nullptr,
-                                            uint8_t* stage1 = nullptr, int arows = 8) {
+                                            uint8_t* stage1 = nullptr, int arows = 8, float* sscl = nullptr,
+                                            const buf_rsrc* rss = nullptr, uint32_t sc_row_off = 0) {
   struct Chunk {
     v8i bf[GPW][NB16];
     v8i af[GPW][MB16];
@@ -543,6 +544,13 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
   // group may stay in flight (the scale loads issued after them can only
   // make this wait longer, never shorter).
   constexpr int NBK = NB16 + MB16, LPC = GPW * 2 * NBK;
+  // Single-stage tiles of one 16-row activation block and 4 groups per wave
+  // stage their scales too: one 4-byte-per-lane DMA brings the 16 rows x 4
+  // groups of a_s (lane l: row l / 4, group l % 4, from the 16-byte run of
+  // the row's 4 consecutive groups) and one more the 4 groups of b_s, into
+  // sscl, in place of 8 scattered loads per wave (decode 64x512x4096: the
+  // scattered loads cost 0.18 us of 4.92).
+  constexpr bool SCL = DMA && ONE != 0 && MB16 == 1 && GPW == 4 && KFIX == 0;
   auto load = [&](Chunk& ch, int c, uint8_t* stage) {
     const int g0 = g_lo + (c * KW + kw) * GPW;
 #pragma unroll
@@ -558,10 +566,17 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
             // ONE == 2: an activation block holds 8 rows, of which the lanes
             // of the tile's arows real rows load theirs; the other rows in
             // LDS stay stale and feed only MFMA rows that are never stored.
-            if (ONE == 2 && b >= NB16) {
+            // Weight rows carry the non-temporal hint: the few workgroups
+            // that share a weight tile (its m-tiles, on one XCD) read it at
+            // about the same time, and nothing reads it later.  (Decode
+            // 64x512x4096: 4.93 -> 4.78 us; the same hint on the activation
+            // rows, which every n-tile re-reads, 6.2 us.)
+            if (b < NB16) {
+              lds_dma16_nt(rsc[0], pd[b][q], k0, base + b * 2048 + q * 1024);
+            } else if (ONE == 2) {
               if (q == 0 && (lane >> 3) < arows) lds_dma16(rsc[1], pd[b][0], k0, base + b * 2048);
             } else {
-              lds_dma16(rsc[b < NB16 ? 0 : 1], pd[b][q], k0, base + b * 2048 + q * 1024);
+              lds_dma16(rsc[1], pd[b][q], k0, base + b * 2048 + q * 1024);
             }
           }
       } else {
@@ -570,9 +585,17 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
 #pragma unroll
         for (int j = 0; j < MB16; ++j) ch.af[u][j] = load_frag_global(pa[j] + k0, lane);
       }
+      if constexpr (!SCL) {
 #pragma unroll
-      for (int j = 0; j < MB16; ++j) ch.as[u][j] = pas[j][g];
-      ch.bs[u] = pbs[g];
+        for (int j = 0; j < MB16; ++j) ch.as[u][j] = pas[j][g];
+        ch.bs[u] = pbs[g];
+      }
+    }
+    if constexpr (SCL) {
+      const int u = lane % GPW;
+      const int g = (g0 + u) < g_hi ? (g0 + u) : (g_hi - 1);
+      lds_dma4(rss[0], sc_row_off + 4u * (uint32_t)g, 0, (lds_u8*)sscl);
+      if (lane < GPW) lds_dma4(rss[1], 4u * (uint32_t)g, 0, (lds_u8*)(sscl + 64));
     }
   };
 
@@ -595,6 +618,10 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
         for (int i = 0; i < NB16; ++i) ch.bf[u][i] = load_frag_lds_sw(base + i * 2048, 0, lane);
 #pragma unroll
         for (int j = 0; j < MB16; ++j) ch.af[u][j] = load_frag_lds_sw(base + (NB16 + j) * 2048, 0, lane);
+        if constexpr (SCL) {
+          ch.as[u][0] = sscl[(lane & 15) * GPW + u];
+          ch.bs[u] = sscl[64 + u];
+        }
       }
     }
 #pragma unroll
@@ -745,6 +772,10 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
   __shared__ __attribute__((aligned(16))) float sRed[KW > 1 && !RED_ALIAS ? KW : 1][RED_ALIAS ? 1 : NBLK][4][64];
   __shared__ __attribute__((aligned(16))) uint8_t sStage0[DMA ? STAGE_H * KW : 16];
   __shared__ __attribute__((aligned(16))) uint8_t sStage1[DMA && !SINGLE ? STAGE_H * KW : 16];
+  // Per-wave scale images of the single-stage tiles: 16 rows x 4 groups of
+  // a_s, then 4 groups of b_s.
+  constexpr bool SCL = DMA && ONE != 0 && MB16 == 1 && GPW == 4 && KFIX == 0;
+  __shared__ __attribute__((aligned(16))) float sScl[SCL ? KW * 80 : 4];
   __shared__ int sLast;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -804,11 +835,19 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
       }
     }
 
+  // Scale-image sources (SCL): lane l reads row m0 + l / 4 (clamped) of a_s,
+  // as an offset from the tile's first row; the group offset is added per
+  // chunk.
+  const buf_rsrc rss[2] = {make_rsrc(a_s + (int64_t)m0 * G), make_rsrc(pbs)};
+  const int srow = m0 + lane / 4;
+  const uint32_t sc_row_off = (uint32_t)((srow < M ? srow : M - 1) - m0) * (uint32_t)G * 4u;
+
   v4f acc[NB16][MB16];
   skinny_tile<NB16, MB16, KW, GPW, KFIX, DMA, ONE>(pb, pa, pas, pbs, g_lo, g_hi, kw, lane, acc, pd, rsc,
                                                    sStage0 + kw * (DMA ? STAGE_H : 0),
                                                    sStage1 + kw * (DMA && !SINGLE ? STAGE_H : 0),
-                                                   M - m0 < 8 ? M - m0 : 8);
+                                                   M - m0 < 8 ? M - m0 : 8, sScl + (SCL ? kw * 80 : 0), rss,
+                                                   sc_row_off);
   // The KW waves' partials, summed in the fixed order kw = 0..KW-1; wave w
   // then owns blocks b with b % KW == w for the rest of the epilogue.
   if constexpr (RED_ALIAS)
