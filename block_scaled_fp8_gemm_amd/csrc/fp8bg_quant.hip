@@ -45,6 +45,22 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)w;
 }
 
+// Streaming accesses: the input is read once and the codes written once, so
+// both carry the non-temporal hint (activation quantiser 16384 x 4096: 38.9
+// -> 35.7 us, interleaved runs).  The weight quantiser takes the hint on its
+// stores only (4096 x 4096: 14.1 -> 10.5 us); on its loads, 256-byte block
+// rows read 16 to a wave, the hint cost 13% (10.6 -> 12.0 us).
+__device__ __forceinline__ uint4 ldg_stream(const uint16_t* p) {
+  typedef unsigned int U4 __attribute__((ext_vector_type(4)));
+  const U4 t = __builtin_nontemporal_load(reinterpret_cast<const U4*>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void stg_stream(uint8_t* p, uint32_t lo, uint32_t hi) {
+  typedef unsigned int U2 __attribute__((ext_vector_type(2)));
+  const U2 t = {lo, hi};
+  __builtin_nontemporal_store(t, reinterpret_cast<U2*>(p));
+}
+
 __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
                                                        float* __restrict__ a_s, int64_t groups) {
   const int lane = threadIdx.x & 63;
@@ -54,7 +70,7 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restric
 #pragma unroll
   for (int u = 0; u < kQuads; ++u) {
     const int64_t g = (wave * kQuads + u) * 4 + sub;
-    raw[u] = g < groups ? *reinterpret_cast<const uint4*>(x + g * 128 + part * 8) : make_uint4(0, 0, 0, 0);
+    raw[u] = g < groups ? ldg_stream(x + g * 128 + part * 8) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int u = 0; u < kQuads; ++u) {
@@ -82,8 +98,7 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restric
       r[i] = clamp448(__builtin_copysignf(__builtin_fmaf(e, y, t), v[i]));
     }
     if (g < groups) {
-      *reinterpret_cast<uint2*>(q + g * 128 + part * 8) =
-          make_uint2(e4m3x4(r[0], r[1], r[2], r[3]), e4m3x4(r[4], r[5], r[6], r[7]));
+      stg_stream(q + g * 128 + part * 8, e4m3x4(r[0], r[1], r[2], r[3]), e4m3x4(r[4], r[5], r[6], r[7]));
       if (part == 0) a_s[g] = s;
     }
   }
@@ -145,8 +160,7 @@ __global__ __launch_bounds__(256) void k_quantize_blocks(const uint16_t* __restr
       r[i] = clamp448(__builtin_copysignf(__builtin_fmaf(e, y, t), v));
     }
     if (n < N)
-      *reinterpret_cast<uint2*>(q + (int64_t)n * K + col) =
-          make_uint2(e4m3x4(r[0], r[1], r[2], r[3]), e4m3x4(r[4], r[5], r[6], r[7]));
+      stg_stream(q + (int64_t)n * K + col, e4m3x4(r[0], r[1], r[2], r[3]), e4m3x4(r[4], r[5], r[6], r[7]));
   }
   if (tid == 0) b_s[blockIdx.x] = s;
 }
