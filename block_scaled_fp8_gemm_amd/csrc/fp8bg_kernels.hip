@@ -354,6 +354,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 #pragma unroll
   for (int j = 0; j < JB; ++j) bf[j] = read_b(0, j);
 
+  // Grouped mode: a wave whose rows all lie past the expert's last row (an
+  // expert of at most 128 tokens in a 256-row tile leaves the second wave row
+  // idle) issues no MFMAs.  It still loads its share of every group and takes
+  // every barrier, in the same order and with the same waits as the full
+  // loop, so the ring's accounting is unchanged; its accumulators stay zero
+  // and its rows are never stored.  The other wave on its SIMD then has the
+  // matrix core to itself (4096 tokens over 256 experts: 257.5 -> 248.2 us;
+  // 2048 tokens in 128 x 256 tiles: 210.0 -> 204.6 us).
+  bool run_full = true;
+  if constexpr (GRP) {
+    static_assert(!MID, "grouped tiles use no mid-group refill");
+    if (m0 + wm * WM >= m_end) {
+      run_full = false;
+      for (int g = 0; g < G; ++g) {
+        const int st = g % STAGES;
+        __builtin_amdgcn_s_waitcnt(vmcnt_only((STAGES - 2) * LPG) & ~(15 << 8));
+        __builtin_amdgcn_s_barrier();
+        issue(grp(g + STAGES), st);
+      }
+    }
+  }
+  if (run_full)
   for (int g = 0; g < G; ++g) {
     const int st = g % STAGES, nst = (g + 1) % STAGES;
     const uint8_t* base = smem + st * STAGE_BYTES;
