@@ -30,6 +30,10 @@ Other modes (for profiles):
   --floors FILE       platform floors: a one-element kernel's launch-to-launch time
                       in graph replays, and device copies of 0.25-256 MiB
   --copy-bytes B      only a plain device copy of B bytes (calibrates HBM counters)
+  --probe-load FILE   the load-path probe (libfp8bg_probe.so): one workgroup per CU
+                      streaming 1 MiB from a shared 256 KiB region (L2 hits) or its
+                      own 1 MiB region (HBM), 4 or 8 waves, direct-to-LDS or register
+                      loads, 8 KB in flight per wave; one JSON line per case to FILE
   --op quantize       time the per-token 1x128 activation quantiser (bf16 -> E4M3
                       codes + fp32 scales) on the workload's A shape instead
   --op quantize_weights   the 128x128 weight-block quantiser on the workload's B shape
@@ -326,6 +330,56 @@ def grouped_alg_bytes(d, out_bytes):
     E, N, K = d["B"].shape
     M, G = d["A"].shape[0], K // 128
     return M * K + 4 * M * G + active * (N * K + 4 * ((N + 127) // 128) * G) + 4 * (E + 1) + M * N * out_bytes
+
+
+def run_probe_load(path, torch):
+    """The load-path probe: per-CU streaming rate of one workgroup per CU."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_scaled_fp8_gemm_amd", "libfp8bg_probe.so"))
+    f = lib.fbg_probe_stream
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    per_wg = 1 << 20
+    shared = torch.zeros(256 << 10, dtype=torch.uint8, device=dev)
+    # two sets of private regions, used in turn: 2 x 256 MiB > the MALL
+    private = [torch.zeros(cu * per_wg, dtype=torch.uint8, device=dev) for _ in range(2)]
+    sink = torch.zeros(cu * 64 * 8, dtype=torch.int32, device=dev)
+    stream = torch.cuda.Stream()
+    reps = 20
+    with open(path, "w") as fh:
+        for src_name in ("l2_shared_256KiB", "hbm_private_1MiB"):
+            for waves in (4, 8):
+                for dma in (1, 0):
+                    loads = per_wg // (waves * 1024)
+
+                    def launch(i):
+                        buf = shared if src_name.startswith("l2") else private[i % 2]
+                        stride = 0 if src_name.startswith("l2") else per_wg
+                        region = shared.numel() if src_name.startswith("l2") else per_wg
+                        st = f(buf.data_ptr(), buf.numel(), stride, region, cu, waves, dma, loads, sink.data_ptr(),
+                               ctypes.c_void_p(stream.cuda_stream))
+                        if st != 0:
+                            raise RuntimeError(f"fbg_probe_stream returned {st}")
+
+                    with torch.cuda.stream(stream):
+                        for i in range(4):
+                            launch(i)
+                        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        t0.record(stream)
+                        for i in range(reps):
+                            launch(i)
+                        t1.record(stream)
+                    torch.cuda.synchronize()
+                    us = t0.elapsed_time(t1) * 1e3 / reps
+                    line = {"probe": "load_path", "source": src_name, "waves": waves,
+                            "loads": "direct-to-LDS" if dma else "registers", "workgroups": cu,
+                            "bytes_per_workgroup": per_wg, "us": round(us, 2),
+                            "gbs_per_cu": round(per_wg / us / 1e3, 1), "tbs_total": round(cu * per_wg / us / 1e6, 2)}
+                    fh.write(json.dumps(line) + "\n")
+                    print(json.dumps(line), flush=True)
 
 
 def run_grouped(args, mw, torch, fbg, W, steps, warmup, use_graph=True, out_name="bf16"):
@@ -637,6 +691,9 @@ def main():
                     help="time only the named workload (the headline line without per_config)")
     ap.add_argument("--out", default=None, help="output dtype (default: the workload's first)")
     ap.add_argument("--M", type=int, default=None, help="a sweep point of the workload")
+    ap.add_argument("--N", type=int, default=None, help="another N for the workload's M and K (tuning)")
+    ap.add_argument("--K", type=int, default=None, help="another K, a multiple of 128 (tuning)")
+    ap.add_argument("--probe-load", default=None, help="the load-path probe, one JSON line per case to FILE")
     ap.add_argument("--max-copies", type=int, default=1024)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -677,6 +734,9 @@ def main():
         return
     if args.floors:
         platform_floors(args.floors, torch)
+        return
+    if args.probe_load:
+        run_probe_load(args.probe_load, torch)
         return
     if args.sweep:
         with open(args.sweep, "w") as f:
@@ -747,6 +807,13 @@ def main():
         return
     w = W.WORKLOADS[args.workload]
     M = args.M if args.M is not None else w.M
+    reshaped = args.N is not None or args.K is not None
+    if reshaped:
+        # Another (N, K) for the workload's inputs recipe: named apart, so no
+        # committed counter record (keyed by workload) applies to it.
+        import dataclasses
+        N_, K_ = args.N or w.N, args.K or w.K
+        w = dataclasses.replace(w, name=f"{w.name}:N{N_}:K{K_}", N=N_, K=K_, sweep_M=())
     if args.op in ("quantize", "quantize_weights"):
         wts = args.op == "quantize_weights"
         r = run_quantize(args, w, M, torch, fbg, args.steps, args.warmup, not args.no_graph, weights=wts)
@@ -772,7 +839,8 @@ def main():
     r = run_workload(args, w, M, out, torch, fbg, W, steps, warmup, not args.no_graph,
                      args.variant, args.split, args.cfg)
     roof = dict(r["roof"])
-    roof["traffic"] = profiled_traffic(w.name, r["plan"], out) if args.cfg is None else None
+    # The committed record is of the workload's own M (and N, K, by name).
+    roof["traffic"] = profiled_traffic(w.name, r["plan"], out) if args.cfg is None and M == w.M else None
     line = {
         "metric": METRIC,
         "value": round(r["tflops"], 3),
@@ -806,14 +874,14 @@ def main():
     d = r.pop("d")
     r_us = r["ms_per_step"]
     del r
-    if w.flops > 1e11 and not args.no_library and args.M is None:
+    if w.flops > 1e11 and not args.no_library and args.M is None and not reshaped:
         # The achievable reference of an MFMA-bound shape, on the same GPU in
         # the same run: the platform library's FP8 GEMM (no block scales).
         lib = library_fp8_gemm(torch, w.M, w.N, w.K)
         ref = {x["scales"]: x["us"] for x in lib if "us" in x}
         line["achievable"] = {"library_fp8_gemm_us": ref,
                               "frac_of_library": {k: round(v / (r_us * 1e3), 4) for k, v in ref.items()}}
-    if not args.no_per_config and args.M is None and args.variant == "auto" and args.cfg is None:
+    if not args.no_per_config and args.M is None and not reshaped and args.variant == "auto" and args.cfg is None:
         line["per_config"] = per_config(args, w.name, out, torch, fbg, W)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(d)

@@ -1,4 +1,6 @@
-"""Builds the HIP library libfp8bg.so in-tree for gfx950 with hipcc.
+"""Builds the HIP library libfp8bg.so in-tree for gfx950 with hipcc, and
+beside it libfp8bg_probe.so, the load-path probe that the benchmark's
+--probe-load mode runs (a measuring tool, not part of the GEMM library).
 
 Every HIP source is compiled for gfx950 only.  Flags:
   -Xclang -target-feature -Xclang -packed-fp32-ops   no packed-FP32 VALU ops
@@ -15,6 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8bg.so")
 SOURCES = ["fp8bg_api.hip", "fp8bg_kernels.hip", "fp8bg_quant.hip", "fp8bg_plan.cpp"]
+PROBE_LIB = os.path.join(PKG, "libfp8bg_probe.so")
+PROBE_SOURCES = ["fp8bg_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -33,11 +37,17 @@ def flags():
 
 
 def build(verbose: bool = False, jobs: int = 3) -> str:
+    lib = _build_lib(SOURCES, LIB, verbose, jobs)
+    _build_lib(PROBE_SOURCES, PROBE_LIB, verbose, jobs)
+    return lib
+
+
+def _build_lib(sources, out, verbose: bool, jobs: int) -> str:
     cc = hipcc()
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     procs, objs = [], []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(objdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         cmd = [cc, *flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -50,18 +60,18 @@ def build(verbose: bool = False, jobs: int = 3) -> str:
     for p, src in procs:
         if p.wait() != 0:
             raise RuntimeError(f"hipcc failed on {src}")
-    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
     # A kernel whose host launch stub was not emitted links fine into a
     # shared library and only fails at load time: refuse it here.
-    nm = subprocess.run(["nm", "-D", "--undefined-only", LIB + ".tmp"], capture_output=True, text=True)
+    nm = subprocess.run(["nm", "-D", "--undefined-only", out + ".tmp"], capture_output=True, text=True)
     missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub" in l]
     if missing:
         raise RuntimeError(f"kernel launch stubs missing from the library: {missing[:3]}")
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
