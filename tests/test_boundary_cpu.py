@@ -396,3 +396,21 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_probe_library_rejects_bad_arguments_before_any_launch():
+    """The load-path probe (a measuring tool beside the library) checks its
+    region against the caller's buffer on the host; a rejected call returns 1
+    and makes no HIP call."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_scaled_fp8_gemm_amd", "libfp8bg_probe.so"))
+    f = lib.fbg_probe_stream
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below is rejected first
+    assert f(None, 1 << 20, 0, 1 << 20, 256, 4, 1, 64, fake, None) == 1           # no source
+    assert f(fake, 1 << 20, 0, 3 << 10, 256, 4, 1, 64, fake, None) == 1           # region not a power of two
+    assert f(fake, 1 << 20, 0, 512, 256, 4, 1, 64, fake, None) == 1               # region below 1 KB
+    assert f(fake, 256 << 20, 1 << 20, 1 << 20, 257, 4, 1, 64, fake, None) == 1   # last region past the buffer
+    assert f(fake, 256 << 20, 1 << 20, 1 << 20, 256, 4, 1, 0, fake, None) == 1    # no loads
+    assert f(fake, 256 << 20, 1 << 20, 1 << 20, 256, 5, 1, 64, fake, None) == 1   # 4 or 8 waves only
