@@ -541,6 +541,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
 // skinny_reduce: sums the KW waves' partials through LDS in the fixed order
 // kw = 0..KW-1; wave w then owns blocks b with b % KW == w.
 // ===========================================================================
+// Single-stage tiles of one 16-row activation block and 4 groups per wave
+// stage their scales through LDS too (skinny_tile's sscl, 80 floats per
+// wave, which the kernel provides exactly when this holds).
+constexpr bool skinny_scales_in_lds(int DMA, int ONE, int MB16, int GPW, int KFIX) {
+  return DMA && ONE != 0 && MB16 == 1 && GPW == 4 && KFIX == 0;
+}
+
 template <int NB16, int MB16, int KW, int GPW, int KFIX, int DMA = 0, int ONE = 0>
 __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint8_t* const* pa,
                                             const float* const* pas, const float* pbs, int g_lo, int g_hi, int kw,
@@ -579,7 +586,7 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
   // the row's 4 consecutive groups) and one more the 4 groups of b_s, into
   // sscl, in place of 8 scattered loads per wave (decode 64x512x4096: the
   // scattered loads cost 0.18 us of 4.92).
-  constexpr bool SCL = DMA && ONE != 0 && MB16 == 1 && GPW == 4 && KFIX == 0;
+  constexpr bool SCL = skinny_scales_in_lds(DMA, ONE, MB16, GPW, KFIX);
   auto load = [&](Chunk& ch, int c, uint8_t* stage) {
     const int g0 = g_lo + (c * KW + kw) * GPW;
 #pragma unroll
@@ -803,7 +810,7 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(
   __shared__ __attribute__((aligned(16))) uint8_t sStage1[DMA && !SINGLE ? STAGE_H * KW : 16];
   // Per-wave scale images of the single-stage tiles: 16 rows x 4 groups of
   // a_s, then 4 groups of b_s.
-  constexpr bool SCL = DMA && ONE != 0 && MB16 == 1 && GPW == 4 && KFIX == 0;
+  constexpr bool SCL = skinny_scales_in_lds(DMA, ONE, MB16, GPW, KFIX);
   __shared__ __attribute__((aligned(16))) float sScl[SCL ? KW * 80 : 4];
   __shared__ int sLast;
 
