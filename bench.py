@@ -76,15 +76,18 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_record(workload):
+def traffic_record(workload, out="bf16"):
     """The machine-readable record of the committed FETCH_SIZE / WRITE_SIZE
-    profile of `workload`, or None."""
+    profile of `workload` with output dtype `out`, or None (a profile file
+    holds one record per output dtype it covers)."""
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     for line in open(path):
         if line.startswith("traffic_record:"):
-            return json.loads(line.split(":", 1)[1])
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("out") == out:
+                return rec
     return None
 
 
@@ -92,7 +95,7 @@ def profiled_traffic(workload, plan, out):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE profile
     of this workload, if that profile was taken on the same kernel sources and
     the same plan; else None."""
-    rec = traffic_record(workload)
+    rec = traffic_record(workload, out)
     if rec is None:
         return None
     same = (rec.get("source_hash") == kernel_source_hash() and rec.get("variant") == plan["variant_name"]
@@ -796,7 +799,7 @@ def main():
         fl = copy_floor_us(r["alg_bytes"], torch)
         line["copy_floor"] = {"us": round(fl, 3), "bytes": r["alg_bytes"],
                               "frac_of_floor": round(fl / (r["ms_per_step"] * 1e3), 4)}
-        rec = traffic_record(mw.name)
+        rec = traffic_record(mw.name, out)
         if (rec is not None and args.cfg is None and rec.get("source_hash") == kernel_source_hash()
                 and rec.get("variant") == "grouped" and rec.get("config") == r["cfg"] and rec.get("out") == out):
             line["roofline"]["traffic"] = rec["traffic_bytes"]

@@ -1,12 +1,16 @@
 """The benchmark's step order (bench.step_schedule, the order time_steps
 runs): every timed use of an input copy must come at least 2x the 256 MB MALL
 of other traffic after that copy's previous use, so no timed step finds its
-operands in the MALL or an L2.  Pure host logic, no GPU."""
+operands in the MALL or an L2.  Also the committed traffic records the
+benchmark reads.  Pure host logic, no GPU."""
 import itertools
+import os
 
 import pytest
 
 import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _check_cold(copies, steps, warmup, use_graph, per_copy):
@@ -65,3 +69,21 @@ def test_per_config_steps_fit_their_copies():
             copies = bench.copies_for(per_copy, 2048)
             assert copies >= 2000 or (copies - 1) * per_copy >= 2 * bench.MALL_BYTES, name
             _check_cold(copies, 2000, 50, True, per_copy)
+
+
+def test_committed_traffic_records_parse_one_per_output_dtype():
+    """Every committed HBM counter profile carries machine-readable records,
+    one per output dtype, that the benchmark finds by workload and dtype."""
+    import glob
+    import json
+    files = glob.glob(os.path.join(ROOT, "profiles", "*_hbm_counters.md"))
+    assert files
+    for path in files:
+        recs = [json.loads(l.split(":", 1)[1]) for l in open(path) if l.startswith("traffic_record:")]
+        assert recs, path
+        outs = [r["out"] for r in recs]
+        assert len(outs) == len(set(outs)), path
+        workload = os.path.basename(path)[: -len("_hbm_counters.md")]
+        for r in recs:
+            assert r["traffic_bytes"] > 0
+            assert bench.traffic_record(workload, r["out"]) == r
