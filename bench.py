@@ -11,8 +11,9 @@ starts.  Steps rotate over input copies such that between two uses of a copy
 the others move at least 2x the 256 MB MALL, and a scrub pass over 1 GiB of
 other memory separates the untimed steps from the timed ones, so every timed
 step reads its operands from HBM (step_schedule gives the exact order).
-Steps are issued from HIP graphs (captured through torch) so that host
-launch cost does not hide the GPU time of a microsecond-scale kernel.  The
+Steps are issued from HIP graphs (captured through torch; one graph holds
+every timed step) so that host launch cost does not hide the GPU time of a
+microsecond-scale kernel.  The
 timed region is bracketed by device synchronisation and by HIP events on the
 stream the kernels run on; ms_per_step and the roofline's per-launch
 duration come from those events.
@@ -130,17 +131,24 @@ def copies_for(per_copy, cap):
     return max(2, min(cap, -(-2 * MALL_BYTES // per_copy) + 1))
 
 
+GRAPH_MAX_STEPS = 4096
+
+
 def chunk_sizes(steps, copies):
-    """The timed steps as graph replays: graphs of one pass over the copies
-    (or of all steps, if fewer), the last one shorter; they add up to `steps`."""
-    chunk = max(1, min(steps, copies))
+    """The timed steps as graph replays: one graph of all steps while they
+    number at most GRAPH_MAX_STEPS (or one pass over the copies, if that is
+    longer), the last one shorter; they add up to `steps`.  Inside a graph
+    the launches run back to back; each further replay would add a gap of
+    ~9 us (kernel traces) that is no part of the kernel."""
+    chunk = max(1, min(steps, max(copies, GRAPH_MAX_STEPS)))
     return [chunk] * (steps // chunk) + ([steps % chunk] if steps % chunk else [])
 
 
 def step_schedule(copies, steps, warmup, use_graph):
     """The order in which time_steps touches the input copies, as a list of
     (phase, copy) pairs: phase "warm" (eager warm-up steps), "replay" (one
-    untimed replay of each captured graph), "scrub" (a pass over SCRUB_BYTES
+    untimed replay of each captured graph, the case where a graph cannot be
+    uploaded instead), "scrub" (a pass over SCRUB_BYTES
     of other memory, copy None) and "timed".  Pure; the CPU tests check on it
     that every timed use of a copy comes at least 2x the MALL after its last
     earlier use."""
@@ -174,11 +182,27 @@ def scrub_mall(stream, torch):
     torch.cuda.synchronize()
 
 
+def upload_graph(graph, stream):
+    """hipGraphUpload of a captured graph, so that its first launch does not
+    pay the upload; False where that cannot be done (the caller then replays
+    the graph once, untimed)."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        f = hip.hipGraphUpload
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        ex = graph.raw_cuda_graph_exec()
+    except (OSError, AttributeError, RuntimeError):
+        return False
+    return bool(ex) and f(ctypes.c_void_p(ex), ctypes.c_void_p(stream.cuda_stream)) == 0
+
+
 def time_steps(step, copies, steps, warmup, use_graph, stream, torch):
     """Runs `warmup` untimed steps, then times exactly `steps` steps with HIP
     events on `stream`, in the order step_schedule gives: replayed from HIP
-    graphs of one pass over the input copies (each graph replayed once,
-    untimed, first) unless use_graph is false, and preceded by a MALL scrub
+    graphs (chunk_sizes; each graph replayed once, untimed, first) unless
+    use_graph is false, and preceded by a MALL scrub
     so that no timed step finds its inputs in a cache.  Returns (GPU ms,
     wall seconds)."""
     with torch.cuda.stream(stream):
@@ -198,8 +222,9 @@ def time_steps(step, copies, steps, warmup, use_graph, stream, torch):
             graphs[n] = g
         plan_seq = [graphs[n] for n in sizes]
         with torch.cuda.stream(stream):   # replay() launches on the current stream
-            for n in sorted(graphs):      # one untimed replay of each graph
-                graphs[n].replay()
+            for n in sorted(graphs):      # uploaded, else replayed once untimed
+                if not upload_graph(graphs[n], stream):
+                    graphs[n].replay()
         torch.cuda.synchronize()
     scrub_mall(stream, torch)
 

@@ -50,9 +50,11 @@ def test_capped_copies_stay_cold_while_steps_fit(use_graph):
 
 
 def test_graph_chunks_add_up():
-    for steps, copies in itertools.product([1, 3, 20, 100, 4097], [2, 3, 4, 211, 2048]):
+    for steps, copies in itertools.product([1, 3, 20, 100, 4097, 9000], [2, 3, 4, 211, 2048, 5000]):
         sizes = bench.chunk_sizes(steps, copies)
-        assert sum(sizes) == steps and max(sizes) <= copies
+        assert sum(sizes) == steps and max(sizes) <= max(copies, bench.GRAPH_MAX_STEPS)
+        if steps <= bench.GRAPH_MAX_STEPS:
+            assert sizes == [steps]   # one graph: no replay gap inside the timed region
 
 
 def test_per_config_steps_fit_their_copies():
