@@ -45,3 +45,14 @@ def test_exact_inputs_are_integers_and_powers_of_two():
     assert np.array_equal(torch_decode(d["B"]), d["Bi"].astype(np.float64))
     assert np.array_equal(d["a_s"], np.exp2(d["u"]).astype(np.float32))
     assert d["b_s"].shape == (2, 2)
+
+
+def test_reshaped_workload_draws_from_its_base_seeds():
+    # bench.py --N/--K renames a workload "<name>:N<n>:K<k>"; its sweep points
+    # must still find a seed (that of the base workload's sweep point)
+    import dataclasses
+    w = W.WORKLOADS["small_16x512x256"]
+    w2 = dataclasses.replace(w, name=w.name + ":N1536:K256", N=1536)
+    assert W.sweep_seed(w2, 32) == W.sweep_seed(w, 32)
+    d = W.make_workload(w2, 32)
+    assert d["A"].shape == (32, 256) and d["B"].shape == (1536, 256)

@@ -70,7 +70,9 @@ ORDER = list(WORKLOADS)
 
 
 def sweep_seed(w: Workload, M: int) -> int:
-    return 100 * (ORDER.index(w.name) + 1) + M
+    # A reshaped workload ("name:N..:K..", the benchmark's tuning runs) draws
+    # from its base workload's seeds.
+    return 100 * (ORDER.index(w.name.split(":")[0]) + 1) + M
 
 
 def groups(K: int) -> int:
