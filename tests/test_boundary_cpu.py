@@ -43,8 +43,9 @@ def test_status_strings():
 
 
 def test_plan_for_the_workloads():
+    # the small case: the swap-AB 16x16 tile (its grid of 32 fits one per CU)
     p = fbg.plan(16, 512, 256)
-    assert p["variant_name"] == "short_k256" and p["split_k"] == 1
+    assert (p["variant_name"], p["config"], p["split_k"], p["grid"]) == ("swap_ab", 2, 1, 32)
     # decode: the single-stage tile of 8 activation rows, unsplit, one
     # workgroup per CU
     p = fbg.plan(64, 512, 4096)
@@ -63,8 +64,17 @@ def test_plan_for_the_workloads():
     # the device)
     p = fbg.plan(32, 512, 16384)
     assert p["variant_name"] == "swap_ab_splitk" and p["split_k"] == 4
-    # K = 256: short-K while its 16x16 grid fits four workgroups per CU or its
-    # 32x16 grid three, the generic kernel beyond (measured faster there)
+    # K = 256: the swap-AB 16x16 tile while its grid is at most one workgroup
+    # per CU (M > 1), then short-K while its 16x16 grid fits four workgroups
+    # per CU or its 32x16 grid three, the generic kernel beyond (measured
+    # faster there)
+    for M, N in ((2, 512), (128, 512), (32, 1536), (16, 4096)):
+        p = fbg.plan(M, N, 256)
+        assert (p["variant_name"], p["config"], p["split_k"]) == ("swap_ab", 2, 1), (M, N)
+        grid = -(-N // 16) * -(-M // 16)
+        assert fbg.plan(M, N, 256, cu_count=128)["variant_name"] == ("swap_ab" if grid <= 128 else "short_k256")
+    assert fbg.plan(1, 512, 256)["variant_name"] == "short_k256"
+    assert fbg.plan(17, 4096, 256)["variant_name"] == "short_k256"
     assert fbg.plan(32, 4096, 256)["variant_name"] == "short_k256"
     assert fbg.plan(128, 1536, 256)["variant_name"] == "short_k256"
     p = fbg.plan(32, 8192, 256)

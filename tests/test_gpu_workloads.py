@@ -63,6 +63,8 @@ def test_workload_sweep(gpu, name, M):
 
 
 @pytest.mark.parametrize("M,N,K,variant,cfg", [
+    (16, 512, 256, "swap_ab", 2),         # K = 256, a 16x16 grid of at most one workgroup per CU
+    (32, 1536, 256, "swap_ab", 2),
     (32, 8192, 256, "short_k256", 12),    # 16x16 short-K tiles, four workgroups per CU
     (256, 1536, 256, "short_k256", 13),   # 32x16 short-K tiles, three per CU
     (4096, 1536, 1024, "generic", 7),     # 128x256 where it ties with 256x128
