@@ -43,8 +43,11 @@ bool env_flag(const char* name) {
 int elem_size(int out_dtype) { return out_dtype == FBG_OUT_FP32 ? 4 : 2; }
 
 // Largest K: the kernels address a tile's rows (up to 256 of K bytes each)
-// with 32-bit offsets from the tile's first row.
-constexpr int64_t kMaxK = (int64_t)1 << 24;
+// through a buffer resource based at the tile's first row, whose 32-bit
+// record count reaches 2^32 - 1 bytes: 256 rows of K bytes must end before
+// that, so K <= 2^24 - 128 (at K = 2^24 the last dword of a 256-row tile
+// read as zero).
+constexpr int64_t kMaxK = ((int64_t)1 << 24) - 128;
 
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   if (!a || !b || abytes <= 0 || bbytes <= 0) return false;

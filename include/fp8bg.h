@@ -91,8 +91,8 @@ typedef struct fbg_plan {
  * 16-byte aligned, a_s and b_s 4-byte aligned, C aligned to its element size.
  * A null pointer with a non-empty extent, a negative size, an unknown
  * out_dtype or a C range that overlaps an input range -> INVALID_VALUE;
- * K % 128 != 0, misalignment, M or N above INT32_MAX, K above 2^24 (the
- * kernels' 32-bit offsets inside a tile's rows), or a scale array of 4 GiB
+ * K % 128 != 0, misalignment, M or N above INT32_MAX, K above 2^24 - 128
+ * (the kernels' 32-bit offsets inside a tile's rows), or a scale array of 4 GiB
  * or more -> UNSUPPORTED.  The dispatcher's variant and tile are used
  * without a K split (the plan of fp8_block_gemm_plan with split_k = 1), so
  * the call needs no workspace and never allocates; it may be captured in a

@@ -203,6 +203,7 @@ def test_host_validation_statuses():
     assert _call(out=3) == fbg.INVALID_VALUE
     assert _call(K=200) == fbg.UNSUPPORTED
     assert _call(K=(1 << 24) + 128) == fbg.UNSUPPORTED      # past the kernels' 32-bit row offsets
+    assert _call(K=1 << 24) == fbg.UNSUPPORTED              # a 256-row tile would end at 2^32 bytes
     assert _call(A=0x10008) == fbg.UNSUPPORTED              # A not 16-byte aligned
     assert _call(B=0x30004) == fbg.UNSUPPORTED
     assert _call(a_s=0x20002) == fbg.UNSUPPORTED
@@ -317,6 +318,7 @@ def test_grouped_host_validation_statuses():
     assert _gcall(out=5) == fbg.INVALID_VALUE
     assert _gcall(K=200) == fbg.UNSUPPORTED
     assert _gcall(K=(1 << 24) + 128) == fbg.UNSUPPORTED
+    assert _gcall(K=1 << 24) == fbg.UNSUPPORTED
     assert _gcall(A=0x100008) == fbg.UNSUPPORTED            # A not 16-byte aligned
     assert _gcall(B=0x300004) == fbg.UNSUPPORTED
     assert _gcall(b_s=0x400002) == fbg.UNSUPPORTED
