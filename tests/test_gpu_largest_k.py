@@ -7,7 +7,8 @@ Integer-valued codes in the first, a middle and the last group of every row
 (zeros elsewhere) and power-of-two scales make every partial exact, so the
 sampled outputs must equal the oracle bit for bit.  (FlagGems-vllm PR #693,
 "feat: optimize w8a8 block fp8 matmul for Hopper", section "Numerical
-safety": the guard admits any K that is a multiple of 128.)
+safety": the guard admits any K that is a multiple of 128.)  Also an output
+of more than 2^31 elements.
 """
 import numpy as np
 import pytest
@@ -52,3 +53,16 @@ def test_largest_k_bitwise_on_edge_rows(gpu, M, N, variant, cfg):
         ref = oracle.block_gemm(d["A"][rows], d["a_s"][rows], d["B"][c:c + 1], d["b_s"][c // 128:c // 128 + 1])
         want = oracle.round_bits(ref, "fp32")[:, 0]
         assert np.array_equal(got[rows, c], want), (variant, cfg, M, N, c, got[rows, c], want)
+
+
+def test_output_past_2_to_31_elements(gpu):
+    """C of 2^32 elements (M = 2^17, N = 2^15): every store index past 2^31
+    must be formed in 64 bits.  Sampled rows, bit for bit in exact mode."""
+    M, N, K2 = 1 << 17, 1 << 15, 128
+    d = workloads.make_exact_inputs(M, N, K2, seed=5)
+    C = run(fbg, to_dev(d), "bf16")
+    rows = [0, 1, 65535, 65536, M - 2, M - 1]
+    got = bits(C[rows], "bf16")
+    del C
+    ref = oracle.block_gemm(d["A"][rows], d["a_s"][rows], d["B"], d["b_s"])
+    assert np.array_equal(got, oracle.round_bits(ref, "bf16"))
