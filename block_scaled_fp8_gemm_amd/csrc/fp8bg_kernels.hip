@@ -129,15 +129,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_generic(
   // switch point.  Issuing all of a group's loads right after one barrier
   // stalls the waves behind the address unit (prefill 288 -> 276 us bf16,
   // 305 -> 294 us fp32, interleaved runs on one box).
-  // LATE_REFILL (2-slot rings, the 256 x 256 tiles): the switch point's
-  // refill is issued after the last row block's MFMAs and next-group B
-  // fragment reads rather than right after the barrier, so those LDS reads
-  // do not queue behind the refill's LDS writes.  Same loads in the same
-  // order; the slot is free from the barrier on.  (Interleaved runs: prefill
-  // 282.5 -> 279.3 and 278.2 -> 274.8 us bf16, 292.4 -> 288.3 us fp32; MoE
-  // 4096 tokens 248.8 -> 240.8 us.  On the 4-slot 64 x 64 tiles at K <= 1024
-  // the later issue cost 1-2%, so they keep the early one.)
-  constexpr bool LATE_REFILL = STAGES == 2;
+  // LATE_REFILL (2- and 3-slot rings): the switch point's refill is issued
+  // after the last row block's MFMAs and next-group B fragment reads rather
+  // than right after the barrier, so those LDS reads do not queue behind the
+  // refill's LDS writes.  Same loads in the same order; the slot is free from
+  // the barrier on.  (Interleaved runs: prefill 282.5 -> 279.3 and 278.2 ->
+  // 274.8 us bf16, 292.4 -> 288.3 us fp32; MoE 4096 tokens 248.8 -> 240.8
+  // us; 3 slots: 1024 x 8192 x 4096 48.1 -> 47.2 us, 4096 x 1536 x 1024
+  // 14.29 -> 14.20, MoE 2048 tokens 203.6 -> 201.0.  On the 4-slot 64 x 64
+  // tiles at K <= 1024 the later issue cost 1-2%, so they keep the early
+  // one.)
+  constexpr bool LATE_REFILL = STAGES <= 3;
   constexpr int A_EARLY = MID ? A_PER_T / 2 : 0;
   constexpr int N_MID = MID ? B_PER_T + 1 + A_EARLY : 0;  // loads per wave issued in the group's second half
   static_assert(!MID || (SCH == 1 && STAGES == 2 && IB >= 6 && A_PER_T % 2 == 0 && WM == 64 * NW / 4 && NW == 8),
