@@ -284,16 +284,17 @@ int make_plan(int64_t M, int64_t N, int64_t K, int out_dtype, int cu_count, int 
   if (v == FBG_VARIANT_AUTO) {
     // K == 256: the swap-AB 16x16 tile (configuration 2, the two groups on
     // two of its four waves) while its grid is at most one workgroup per CU
-    // and M > 1, then short-K while its 16x16 or 32x16 grid fits, else
-    // generic.  The swap-AB tile measured 1-3% faster there (interleaved
-    // runs, cold: 16x512x256 3.00 against 3.11 us for short-K, 32x512
-    // 3.00 / 3.09, 64x512 3.02 / 3.07, 16x1536 3.05 / 3.09; dispatch sweep:
-    // 128x512, 32x1536, 16x4096 likewise), and not at M = 1 (1536 and 4096
-    // columns 0.6-0.8% slower) or past one workgroup per CU (32x4096 3.35
+    // (for M = 1 only up to 512 columns), then short-K while its 16x16 or
+    // 32x16 grid fits, else generic.  The swap-AB tile measured 1-4% faster
+    // there (interleaved runs, cold: 16x512x256 3.00 against 3.11 us for
+    // short-K, 32x512 3.00 / 3.09, 64x512 3.02 / 3.07, 16x1536 3.05 / 3.09;
+    // dispatch sweeps: 128x512, 32x1536, 16x4096 likewise, 1x512 2.87-2.89
+    // against 2.96-2.99 in three runs), and not at M = 1 with 1536 or 4096
+    // columns (0.6-0.8% slower) or past one workgroup per CU (32x4096 3.35
     // against 3.21).  Otherwise swap-AB for M <= 16 and, up to M = 512, when
     // swap_pick finds a tile; the generic kernel for the rest.
     if (K == 256 && M <= 1024)
-      v = (M > 1 && cdiv(N, 16) * cdiv(M, 16) <= (int64_t)cu) ? FBG_VARIANT_SWAP_AB
+      v = ((M > 1 || N <= 512) && cdiv(N, 16) * cdiv(M, 16) <= (int64_t)cu) ? FBG_VARIANT_SWAP_AB
           : short_fits(M, N, cu)                             ? FBG_VARIANT_SHORT_K256
                                                              : FBG_VARIANT_GENERIC;
     else if (M <= 16 || (M <= 512 && picked))

@@ -73,7 +73,8 @@ def test_plan_for_the_workloads():
         assert (p["variant_name"], p["config"], p["split_k"]) == ("swap_ab", 2, 1), (M, N)
         grid = -(-N // 16) * -(-M // 16)
         assert fbg.plan(M, N, 256, cu_count=128)["variant_name"] == ("swap_ab" if grid <= 128 else "short_k256")
-    assert fbg.plan(1, 512, 256)["variant_name"] == "short_k256"
+    assert fbg.plan(1, 512, 256)["variant_name"] == "swap_ab"      # one token: only up to 512 columns
+    assert fbg.plan(1, 1536, 256)["variant_name"] == "short_k256"
     assert fbg.plan(17, 4096, 256)["variant_name"] == "short_k256"
     assert fbg.plan(32, 4096, 256)["variant_name"] == "short_k256"
     assert fbg.plan(128, 1536, 256)["variant_name"] == "short_k256"
