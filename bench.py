@@ -201,8 +201,9 @@ def upload_graph(graph, stream):
 def time_steps(step, copies, steps, warmup, use_graph, stream, torch):
     """Runs `warmup` untimed steps, then times exactly `steps` steps with HIP
     events on `stream`, in the order step_schedule gives: replayed from HIP
-    graphs (chunk_sizes; each graph replayed once, untimed, first) unless
-    use_graph is false, and preceded by a MALL scrub
+    graphs (chunk_sizes; each graph uploaded first, or where that is not
+    available replayed once, untimed) unless use_graph is false, and
+    preceded by a MALL scrub
     so that no timed step finds its inputs in a cache.  Returns (GPU ms,
     wall seconds)."""
     with torch.cuda.stream(stream):
