@@ -607,7 +607,16 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
       // Single-stage tiles issue all of a chunk's weight-row loads (from
       // HBM) before its activation-row loads (mostly L2 hits), rather than
       // group by group (decode 64x512x4096: 4.91 -> 4.84 us; the 16x16 tile
-      // 5.30 -> 5.10 us; 32x512x4096 4.83 -> 4.72 us; interleaved runs).
+      // 5.30 -> 5.10 us; 32x512x4096 4.83 -> 4.72 us; interleaved runs; the
+      // same order in the two-slot tiles measured no different).
+      // Weight rows carry the non-temporal hint: the few workgroups that
+      // share a weight tile (its m-tiles, on one XCD) read it at about the
+      // same time, and nothing reads it later.  (Decode 64x512x4096: 4.93 ->
+      // 4.78 us; the same hint on the activation rows, which every n-tile
+      // re-reads, 6.2 us.)  With ONE == 2 an activation block holds 8 rows,
+      // of which the lanes of the tile's arows real rows load theirs; the
+      // other rows in LDS stay stale and feed only MFMA rows that are never
+      // stored.
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -651,18 +660,10 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
         for (int b = 0; b < NBK; ++b)
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            // ONE == 2: an activation block holds 8 rows, of which the lanes
-            // of the tile's arows real rows load theirs; the other rows in
-            // LDS stay stale and feed only MFMA rows that are never stored.
-            // Weight rows carry the non-temporal hint: the few workgroups
-            // that share a weight tile (its m-tiles, on one XCD) read it at
-            // about the same time, and nothing reads it later.  (Decode
-            // 64x512x4096: 4.93 -> 4.78 us; the same hint on the activation
-            // rows, which every n-tile re-reads, 6.2 us.)
+            // Weight rows carry the non-temporal hint, as in the single-stage
+            // tiles above.
             if (b < NB16) {
               lds_dma16_nt(rsc[0], pd[b][q], k0, base + b * 2048 + q * 1024);
-            } else if (ONE == 2) {
-              if (q == 0 && (lane >> 3) < arows) lds_dma16(rsc[1], pd[b][0], k0, base + b * 2048);
             } else {
               lds_dma16(rsc[1], pd[b][q], k0, base + b * 2048 + q * 1024);
             }
