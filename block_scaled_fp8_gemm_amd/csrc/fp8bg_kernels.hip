@@ -651,35 +651,35 @@ __device__ __forceinline__ void skinny_tile(const uint8_t* const* pb, const uint
       }
     } else {
 #pragma unroll
-    for (int u = 0; u < GPW; ++u) {
-      const int g = (g0 + u) < g_hi ? (g0 + u) : (g_hi - 1);
-      const int k0 = g * kGroup;
-      if constexpr (DMA) {
-        lds_u8* base = (lds_u8*)(stage + u * NBK * 2048);
+      for (int u = 0; u < GPW; ++u) {
+        const int g = (g0 + u) < g_hi ? (g0 + u) : (g_hi - 1);
+        const int k0 = g * kGroup;
+        if constexpr (DMA) {
+          lds_u8* base = (lds_u8*)(stage + u * NBK * 2048);
 #pragma unroll
-        for (int b = 0; b < NBK; ++b)
+          for (int b = 0; b < NBK; ++b)
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            // Weight rows carry the non-temporal hint, as in the single-stage
-            // tiles above.
-            if (b < NB16) {
-              lds_dma16_nt(rsc[0], pd[b][q], k0, base + b * 2048 + q * 1024);
-            } else {
-              lds_dma16(rsc[1], pd[b][q], k0, base + b * 2048 + q * 1024);
+            for (int q = 0; q < 2; ++q) {
+              // Weight rows carry the non-temporal hint, as in the single-stage
+              // tiles above.
+              if (b < NB16) {
+                lds_dma16_nt(rsc[0], pd[b][q], k0, base + b * 2048 + q * 1024);
+              } else {
+                lds_dma16(rsc[1], pd[b][q], k0, base + b * 2048 + q * 1024);
+              }
             }
-          }
-      } else {
+        } else {
 #pragma unroll
-        for (int i = 0; i < NB16; ++i) ch.bf[u][i] = load_frag_global(pb[i] + k0, lane);
+          for (int i = 0; i < NB16; ++i) ch.bf[u][i] = load_frag_global(pb[i] + k0, lane);
 #pragma unroll
-        for (int j = 0; j < MB16; ++j) ch.af[u][j] = load_frag_global(pa[j] + k0, lane);
+          for (int j = 0; j < MB16; ++j) ch.af[u][j] = load_frag_global(pa[j] + k0, lane);
+        }
+        if constexpr (!SCL) {
+#pragma unroll
+          for (int j = 0; j < MB16; ++j) ch.as[u][j] = pas[j][g];
+          ch.bs[u] = pbs[g];
+        }
       }
-      if constexpr (!SCL) {
-#pragma unroll
-        for (int j = 0; j < MB16; ++j) ch.as[u][j] = pas[j][g];
-        ch.bs[u] = pbs[g];
-      }
-    }
     }
     if constexpr (SCL) {
       const int u = lane % GPW;
