@@ -63,7 +63,25 @@ def grouped_cases(n=200, seed=98):
     return out
 
 
+def single_stage_cases(n=300, seed=99):
+    """The single-stage swap-AB tiles (configurations 22 and 23: every load of
+    a workgroup in flight at once, weight rows issued before activation rows),
+    on ragged M and N and on group counts that leave partial chunks."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.choice([rng.integers(1, 20), rng.integers(20, 130), rng.integers(130, 400)]))
+        N = int(rng.choice([rng.integers(1, 200), rng.integers(200, 1100)]))
+        K = int(128 * rng.integers(1, 41))
+        if M * N * K > 2e8:
+            continue
+        out.append((M, N, K, "swap_ab", int(rng.choice([22, 23])), 0,
+                    str(rng.choice(["bf16", "fp16", "fp32"])), int(rng.integers(1 << 30))))
+    return out
+
+
 DENSE = dense_cases()
+SINGLE = single_stage_cases()
 GROUPED = grouped_cases()
 
 
@@ -73,10 +91,9 @@ def test_the_draws_cover_every_variant_and_many_configurations():
     assert len({c[3] for c in GROUPED}) >= 15
 
 
-@pytest.mark.parametrize("chunk", range(len(DENSE) // CHUNK))
-def test_random_forced_dense_bitwise(gpu, chunk):
+def run_dense_chunk(cases):
     ran = 0
-    for M, N, K, variant, cfg, S, out, seed in DENSE[chunk * CHUNK:(chunk + 1) * CHUNK]:
+    for M, N, K, variant, cfg, S, out, seed in cases:
         what = f"{M}x{N}x{K} {variant} cfg={cfg} S={S} {out} seed={seed}"
         d = workloads.make_exact_inputs(M, N, K, seed=seed)
         try:
@@ -86,7 +103,17 @@ def test_random_forced_dense_bitwise(gpu, chunk):
             continue
         assert_bitwise(C, oracle.block_gemm(d["A"], d["a_s"], d["B"], d["b_s"]), out, what)
         ran += 1
-    assert ran > 0
+    return ran
+
+
+@pytest.mark.parametrize("chunk", range(len(DENSE) // CHUNK))
+def test_random_forced_dense_bitwise(gpu, chunk):
+    assert run_dense_chunk(DENSE[chunk * CHUNK:(chunk + 1) * CHUNK]) > 0
+
+
+@pytest.mark.parametrize("chunk", range(len(SINGLE) // (3 * CHUNK)))
+def test_random_single_stage_bitwise(gpu, chunk):
+    assert run_dense_chunk(SINGLE[chunk * 3 * CHUNK:(chunk + 1) * 3 * CHUNK]) == 3 * CHUNK
 
 
 @pytest.mark.parametrize("chunk", range(len(GROUPED) // CHUNK))
